@@ -1,0 +1,173 @@
+/*
+ * ragged_prefill.h — C ABI of the MI355X (gfx950) ragged prefill attention library.
+ *
+ * The operation (page "Module flashinfer", module doc and functions
+ * ragged_prefill_bf16_hd128 / ragged_prefill_bf16_hd256): N requests of
+ * different lengths, located in packed buffers by q_indptr / kv_indptr ragged
+ * offsets, run their attention in ONE launch,
+ *
+ *     O = softmax(sm_scale * Q K^T + mask) V
+ *
+ * in BF16 with grouped-query heads (num_qo_heads a multiple of num_kv_heads,
+ * qo head h reads kv head h / (num_qo_heads / num_kv_heads)), head_dim 128 or
+ * 256, causal selectable.  The causal mask is aligned to the end of each
+ * request's KV (bottom-right; page "flashinfer-ai/flashinfer", benchmarks
+ * README, attention flag --causal): key j is visible to query row i of a
+ * request iff j <= i + kv_len - qo_len.  The library also returns the per-row
+ * log-sum-exp (the *_return_lse prefill entry points, page
+ * "flashinfer-ai/flashinfer", attention API, single request prefill).
+ *
+ * Layouts (packed NHD, contiguous, device memory, 16-byte aligned base):
+ *   q, o : bf16 [total_q,  num_qo_heads, head_dim]
+ *   k, v : bf16 [total_kv, num_kv_heads, head_dim]
+ *   lse  : fp32 [total_q,  num_qo_heads], natural log of sum_j exp(s_j) over
+ *          the visible keys, s_j = sm_scale * q.k_j.  May be NULL.
+ *   q_indptr, kv_indptr : HOST int32 [batch + 1], non-decreasing, >= 0;
+ *          request b owns q rows [q_indptr[b], q_indptr[b+1]) and kv rows
+ *          [kv_indptr[b], kv_indptr[b+1]); q_indptr[0] need not be 0.
+ *
+ * Conventions:
+ *   - Rows outside every request are never written.  A request with
+ *     qo_len = 0 writes nothing.
+ *   - A query row that sees no key (kv_len = 0, or causal with
+ *     i < qo_len - kv_len) gets O = +0 and LSE = -inf.
+ *   - batch == 0 or total_q == 0 returns RP_OK without launching anything
+ *     (the empty-batch early return of page "vllm-rlt PR #112", design notes).
+ *   - Output rounding: fp32 -> bf16 round-to-nearest-even, once.
+ *   - Per-request results are bit-for-bit independent of the other requests
+ *     in the batch and of how the planner places the work.
+ *   - All device work is enqueued on `stream` (a hipStream_t; NULL = the
+ *     null stream).  Asynchronous device faults surface at the caller's next
+ *     synchronisation.
+ *   - Nothing throws across this boundary; every entry point returns a
+ *     status.  rp_last_error() gives a thread-local description of the last
+ *     failure.
+ *
+ * Ownership: the caller owns q, k, v, o, lse, the indptr arrays and the
+ * stream; the library never frees them.  A plan owns its host metadata and its
+ * device-resident worklist; destroy it only after the stream work that uses it
+ * has completed.  The workspace of the two-phase API is caller-provided (the
+ * "instance-owned workspace" of page "vllm-rlt PR #112", design notes and
+ * review); the one-shot call grows a per-device workspace of its own on first
+ * use and keeps it until the process ends.
+ */
+#ifndef RAGGED_PREFILL_H
+#define RAGGED_PREFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RP_ABI_VERSION 1
+
+/* Status codes. */
+enum rp_status {
+    RP_OK = 0,
+    RP_EINVAL = -1,        /* malformed argument (pointer, shape, offsets, scale) */
+    RP_EUNSUPPORTED = -2,  /* valid but not supported (head_dim, device) */
+    RP_ENOMEM = -3,        /* host or device allocation failed; outputs untouched */
+    RP_EDEVICE = -4        /* a HIP runtime call or a launch failed */
+};
+
+/* Static text for a status code; never NULL. */
+const char *rp_status_string(int status);
+
+/* Thread-local text describing the last failure on this thread ("" if none). */
+const char *rp_last_error(void);
+
+/* RP_ABI_VERSION of the loaded library. */
+int rp_abi_version(void);
+
+/* 1 if the current HIP device is a gfx950 and the kernels are loadable, else 0
+ * (the available() gate of page "Module flashinfer", functions). */
+int rp_available(void);
+
+/*
+ * One-shot call: plans and runs on `stream` (the ragged_prefill_bf16_hd128 /
+ * _hd256 FFI of page "Module flashinfer", with head_dim an argument).
+ * head_dim must be 128 or 256; num_qo_heads % num_kv_heads == 0;
+ * sm_scale finite.  Plans are cached per (offsets, shape); the device
+ * worklist upload of a new plan and the growth of the library-owned
+ * workspace synchronise with the device once.  Not safe to call from several
+ * host threads at once on one device: use the two-phase API for that.
+ */
+int ragged_prefill_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
+                        const int32_t *q_indptr, const int32_t *kv_indptr, int batch,
+                        int num_qo_heads, int num_kv_heads, int head_dim, int causal,
+                        float sm_scale, void *stream);
+
+/* ---- Two-phase API: plan once per batch shape, run many times ---------------
+ * ("preparation once per KV batch", page "vllm-rlt PR #112", review item 3.)
+ */
+
+typedef struct rp_plan rp_plan;
+
+enum rp_split_mode {
+    RP_SPLIT_AUTO = 0,    /* split long KV across workgroups only when the batch is small */
+    RP_SPLIT_NEVER = 1,   /* one workgroup per tile, folding KV chunks in order */
+    RP_SPLIT_ALWAYS = 2   /* one workgroup per (tile, KV chunk) + merge kernel */
+};
+
+/* Planner options.  All-zero means defaults.  The KV chunk size fixes the
+ * numerics (where partial states are cut and merged); the split mode only
+ * moves work between workgroups and never changes a bit of the results. */
+typedef struct rp_plan_opts {
+    int kv_chunk;    /* canonical KV chunk in keys (multiple of 64, >= 64); 0 = default 2048 */
+    int split_mode;  /* enum rp_split_mode */
+    int host_only;   /* nonzero: plan on the host only; such a plan can be inspected, not run */
+    int reserved;
+} rp_plan_opts;
+
+/* Summary of a plan (host side). */
+typedef struct rp_plan_info {
+    int64_t num_items;         /* tile work items (workgroups of the tile kernel) */
+    int64_t num_partial_items; /* of which write fp32 partial states */
+    int64_t num_merge_items;   /* merge kernel workgroups (tiles with partial states) */
+    int64_t total_q;           /* sum of qo_len */
+    int64_t total_kv;          /* sum of kv_len */
+    int32_t tile_rows;         /* rows (token x qo-head pairs) per tile */
+    int32_t tile_tokens;       /* tokens per tile */
+    int32_t key_block;         /* keys per inner-loop block */
+    int32_t kv_chunk;          /* canonical KV chunk, keys */
+    double flops;              /* algorithmic: 4 * head_dim * num_qo_heads * visible pairs */
+    double bytes;              /* algorithmic: Q,K,V read once, O,LSE written once */
+    size_t workspace_bytes;    /* bytes rp_run needs (0 if no partial states) */
+} rp_plan_info;
+
+/* Build a plan from HOST offsets.  On success *out owns a plan (possibly with
+ * zero items for an empty batch).  Unless opts->host_only, the worklist is
+ * copied to the current device (synchronously). */
+int rp_plan_create(const int32_t *q_indptr, const int32_t *kv_indptr, int batch,
+                   int num_qo_heads, int num_kv_heads, int head_dim, int causal,
+                   const rp_plan_opts *opts, rp_plan **out);
+
+int rp_plan_get_info(const rp_plan *plan, rp_plan_info *info);
+
+/* Device workspace bytes rp_run needs for this plan (0 = none). */
+size_t rp_plan_workspace_bytes(const rp_plan *plan);
+
+/* Host copy of the tile worklist: RP_ITEM_INTS int32 per item, in launch
+ * order (for inspection and tests).  capacity counts items. Returns the number
+ * of items copied (>= 0) or a negative status. */
+#define RP_ITEM_INTS 16
+int64_t rp_plan_copy_items(const rp_plan *plan, int32_t *dst, int64_t capacity);
+
+/* Run a plan on `stream`.  workspace: device memory of at least
+ * rp_plan_workspace_bytes(plan) bytes, 256-byte aligned (may be NULL when that
+ * is 0).  Launches one tile kernel, plus one merge kernel when the plan holds
+ * partial states.  Captures into a HIP graph (no allocation, no host sync, no
+ * memset). */
+int rp_run(const rp_plan *plan, const void *q, const void *k, const void *v, void *o,
+           float *lse, float sm_scale, void *workspace, size_t workspace_bytes,
+           void *stream);
+
+void rp_plan_destroy(rp_plan *plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RAGGED_PREFILL_H */

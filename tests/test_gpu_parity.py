@@ -1,0 +1,251 @@
+"""GPU path against the fp64 oracle (needs an MI355X).
+
+Every case draws its inputs from the seeded generator in ``workloads``, runs
+the HIP library through its C ABI (via the ctypes binding), and checks the
+result element by element against ``oracle`` (see tests/parity.py for the
+gates).  Invariant and determinism cases compare GPU results with each other
+bit for bit.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import bf16_to_f64, compare, default_scale
+from workloads import get_config, make_batch, make_config_batch
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import varlen_prefill_amd as vp
+    assert vp.available(), "the gfx950 library did not load or the device is not a gfx950"
+
+
+def _gpu(batch, causal, sm_scale, fill=float("nan"), **plan_kw):
+    """Run one batch through a fresh plan; outputs pre-filled with `fill`."""
+    import varlen_prefill_amd as vp
+    q, k, v = batch.q.to(DEV), batch.k.to(DEV), batch.v.to(DEV)
+    out = torch.full_like(q, fill)
+    lse = torch.full((q.shape[0], batch.num_qo_heads), fill, dtype=torch.float32, device=DEV)
+    plan = vp.Plan(batch.q_indptr, batch.kv_indptr, batch.num_qo_heads, batch.num_kv_heads,
+                   batch.head_dim, causal, **plan_kw)
+    plan.run(q, k, v, out=out, lse=lse, sm_scale=sm_scale)
+    torch.cuda.synchronize()
+    plan.close()
+    return out.cpu(), lse.cpu()
+
+
+def _oracle(batch, causal, sm_scale):
+    return oracle.ragged_attention(batch.q, batch.k, batch.v, batch.q_indptr, batch.kv_indptr,
+                                   batch.num_qo_heads, batch.num_kv_heads, causal, sm_scale)
+
+
+def _rows_in_requests(batch):
+    rows = np.zeros(batch.q.shape[0], dtype=bool)
+    for r in range(batch.batch):
+        rows[int(batch.q_indptr[r]):int(batch.q_indptr[r + 1])] = True
+    return rows
+
+
+def _check_full(batch, causal, sm_scale, **plan_kw):
+    o, lse = _gpu(batch, causal, sm_scale, **plan_kw)
+    ro, rl = _oracle(batch, causal, sm_scale)
+    rows = _rows_in_requests(batch)
+    rep = compare(bf16_to_f64(o)[rows], lse.double().numpy()[rows], ro[rows], rl[rows])
+    # rows outside every request are never written
+    assert torch.isnan(o[~torch.from_numpy(rows)]).all()
+    assert torch.isnan(lse[~torch.from_numpy(rows)]).all()
+    print(rep)
+    return o, lse, rep
+
+
+def test_tiny_config():
+    cfg = get_config("tiny")
+    b = make_config_batch(cfg)
+    _check_full(b, cfg.causal, default_scale(cfg.head_dim))
+
+
+CASES = [
+    # (qo_lens, kv_lens, Hq, Hkv, D, causal)
+    ([1, 130, 257, 64], [1, 130, 257, 64], 8, 2, 128, True),          # several tiles, ragged tails
+    ([300, 5, 77], [300, 5, 77], 4, 4, 128, True),                      # MHA (g = 1), 128-token tiles
+    ([40, 0, 1, 200], [90, 3, 1, 200], 8, 1, 128, False),               # g = 8, non-causal, qo != kv
+    ([33, 129, 7], [500, 129, 2], 16, 2, 128, True),                    # append (qo < kv), qo > kv rows
+    ([100, 3, 0], [0, 3, 5], 4, 2, 128, True),                          # kv = 0, zero-length request
+    ([1, 130, 257, 64], [1, 130, 257, 64], 8, 2, 256, True),            # hd256
+    ([70, 150], [300, 150], 4, 2, 256, False),                          # hd256 non-causal
+    ([45, 12], [45, 300], 12, 4, 128, True),                            # g = 3 (padding rows)
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_small_ragged(case):
+    qo, kv, hq, hkv, d, causal = CASES[case]
+    b = make_batch(qo, kv, hq, hkv, d, seed=1000 + case, q_base=3, kv_base=5)
+    _check_full(b, causal, default_scale(d))
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_split_kv_chunks(d):
+    # a small canonical chunk forces split tiles + the merge kernel
+    b = make_batch([50, 300, 9], [700, 300, 1000], 8, 2, d, seed=2000 + d)
+    for causal in (True, False):
+        _check_full(b, causal, default_scale(d), kv_chunk=128)
+
+
+def test_batch_composition_bitwise():
+    lens_q = [130, 0, 1, 257, 64, 600]
+    lens_kv = [130, 7, 1, 400, 64, 600]
+    sm = default_scale(128)
+    for kv_chunk in (0, 192):
+        full = make_batch(lens_q, lens_kv, 8, 2, 128, seed=77)
+        fo, fl = _gpu(full, True, sm, kv_chunk=kv_chunk)
+        perm = [5, 3, 0, 2, 4, 1]
+        pb = make_batch([lens_q[i] for i in perm], [lens_kv[i] for i in perm], 8, 2, 128, seed=77,
+                        request_ids=perm)
+        po, pl = _gpu(pb, True, sm, kv_chunk=kv_chunk)
+        for r in range(len(lens_q)):
+            alone = make_batch([lens_q[r]], [lens_kv[r]], 8, 2, 128, seed=77, request_ids=[r])
+            ao, al = _gpu(alone, True, sm, kv_chunk=kv_chunk)
+            q0, q1 = int(full.q_indptr[r]), int(full.q_indptr[r + 1])
+            pos = perm.index(r)
+            p0, p1 = int(pb.q_indptr[pos]), int(pb.q_indptr[pos + 1])
+            assert torch.equal(ao.view(torch.int16), fo[q0:q1].view(torch.int16))
+            assert torch.equal(al.view(torch.int32), fl[q0:q1].view(torch.int32))
+            assert torch.equal(po[p0:p1].view(torch.int16), fo[q0:q1].view(torch.int16))
+            assert torch.equal(pl[p0:p1].view(torch.int32), fl[q0:q1].view(torch.int32))
+
+
+def test_split_mode_always_matches_auto_bitwise():
+    import varlen_prefill_amd as vp
+    b = make_batch([200, 31], [3000, 31], 8, 2, 128, seed=5)
+    ao, al = _gpu(b, True, default_scale(128), kv_chunk=1024)
+    so, sl = _gpu(b, True, default_scale(128), kv_chunk=1024, split_mode=vp.RP_SPLIT_ALWAYS)
+    assert torch.equal(ao.view(torch.int16), so.view(torch.int16))
+    assert torch.equal(al.view(torch.int32), sl.view(torch.int32))
+
+
+def test_repeat_runs_bitwise():
+    import varlen_prefill_amd as vp
+    b = make_batch([300, 45], [300, 1000], 8, 2, 128, seed=6)
+    q, k, v = b.q.to(DEV), b.k.to(DEV), b.v.to(DEV)
+    plan = vp.Plan(b.q_indptr, b.kv_indptr, 8, 2, 128, True, kv_chunk=256)
+    o0, l0 = plan.run(q, k, v)
+    o0, l0 = o0.clone(), l0.clone()
+    for _ in range(10):
+        o1, l1 = plan.run(q, k, v)
+        assert torch.equal(o1.view(torch.int16), o0.view(torch.int16))
+        assert torch.equal(l1.view(torch.int32), l0.view(torch.int32))
+    plan.close()
+
+
+def test_closed_forms_on_gpu():
+    import varlen_prefill_amd as vp
+    d = 128
+    # kv_len = 1 -> O = V[0] exactly; causal qo = kv -> row 0 = V[0] exactly
+    b = make_batch([5, 70], [1, 70], 8, 2, d, seed=8)
+    o, _ = _gpu(b, False, default_scale(d))
+    assert torch.equal(o[0:5].float(), b.v[0:1].float().repeat_interleave(4, 1).expand(5, 8, d))
+    o, _ = _gpu(b, True, default_scale(d))
+    assert torch.equal(o[5].float(), b.v[1].float().repeat_interleave(4, 0))
+    # sm_scale = 0 -> mean of the visible V rows; LSE = ln(#visible)
+    b = make_batch([9, 200], [9, 300], 4, 2, d, seed=9)
+    o, lse = _gpu(b, True, 0.0)
+    ro, rl = _oracle(b, True, 0.0)
+    compare(bf16_to_f64(o), lse.double().numpy(), ro, rl)
+    # negative scale goes through the same definition
+    o, lse = _gpu(b, True, -0.05)
+    ro, rl = _oracle(b, True, -0.05)
+    compare(bf16_to_f64(o), lse.double().numpy(), ro, rl)
+
+
+def test_one_shot_entry_point_and_streams():
+    import varlen_prefill_amd as vp
+    cfg = get_config("tiny")
+    b = make_config_batch(cfg)
+    q, k, v = b.q.to(DEV), b.k.to(DEV), b.v.to(DEV)
+    ro, rl = _oracle(b, True, default_scale(128))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o, lse = vp.ragged_prefill(q, k, v, b.q_indptr, b.kv_indptr, causal=True)
+    s.synchronize()
+    compare(bf16_to_f64(o.cpu()), lse.cpu().double().numpy(), ro, rl)
+    o2, lse2 = vp.ragged_prefill(q, k, v, torch.from_numpy(b.q_indptr).to(DEV),
+                                 torch.from_numpy(b.kv_indptr).to(DEV), causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.cpu().view(torch.int16), o.cpu().view(torch.int16))
+    # empty batch: returns without launching
+    e = torch.empty(0, 4, 128, dtype=torch.bfloat16, device=DEV)
+    ek = torch.empty(0, 2, 128, dtype=torch.bfloat16, device=DEV)
+    vp.ragged_prefill(e, ek, ek, [0], [0])
+
+
+def test_graph_capture_replays():
+    import varlen_prefill_amd as vp
+    b = make_batch([150, 20], [900, 20], 8, 2, 128, seed=12)
+    q, k, v = b.q.to(DEV), b.k.to(DEV), b.v.to(DEV)
+    plan = vp.Plan(b.q_indptr, b.kv_indptr, 8, 2, 128, True, kv_chunk=256)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[0], 8, dtype=torch.float32, device=DEV)
+    ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=DEV)
+    plan.run(q, k, v, out=out, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    ref_o, ref_l = out.clone(), lse.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            plan.run(q, k, v, out=out, lse=lse, workspace=ws, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    for _ in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_o.view(torch.int16))
+        assert torch.equal(lse.view(torch.int32), ref_l.view(torch.int32))
+    plan.close()
+
+
+@pytest.mark.parametrize("name", ["hd128_gqa_causal", "ragged64"])
+def test_full_size_config_sampled(name):
+    """Full-size workloads in the benchmark's launch configuration: every head
+    of the first/last 40 tokens of each request and 3000 random rows are
+    checked against the oracle row by row."""
+    cfg = get_config(name)
+    b = make_config_batch(cfg)
+    sm = default_scale(cfg.head_dim)
+    o, lse = _gpu(b, cfg.causal, sm)
+    rng = np.random.default_rng(123)
+    toks = []
+    for r in range(b.batch):
+        q0, q1 = int(b.q_indptr[r]), int(b.q_indptr[r + 1])
+        toks += list(range(q0, min(q1, q0 + 40))) + list(range(max(q0, q1 - 40), q1))
+    toks = np.unique(np.array(toks, dtype=np.int64))
+    tt = np.repeat(toks, cfg.num_qo_heads)
+    hh = np.tile(np.arange(cfg.num_qo_heads), toks.size)
+    total = int(b.q_indptr[-1])
+    rt = rng.integers(0, total, 3000)
+    rh = rng.integers(0, cfg.num_qo_heads, 3000)
+    tt = np.concatenate([tt, rt])
+    hh = np.concatenate([hh, rh])
+    ro, rl = oracle.ragged_attention_rows(b.q, b.k, b.v, b.q_indptr, b.kv_indptr,
+                                          cfg.num_qo_heads, cfg.num_kv_heads, cfg.causal, sm,
+                                          tt, hh)
+    og = bf16_to_f64(o)[tt, hh]
+    lg = lse.double().numpy()[tt, hh]
+    print(compare(og, lg, ro, rl))
+    assert not torch.isnan(o).any() and not torch.isnan(lse).any()

@@ -1,0 +1,238 @@
+"""Ragged (varlen) batched prefill attention for MI355X (gfx950).
+
+    O = softmax(sm_scale * Q K^T + causal mask) V   over N ragged requests in one launch,
+
+BF16 with grouped-query heads, head_dim 128 or 256, causal selectable (bottom-right
+aligned), with the per-row log-sum-exp.  The computation runs in the HIP library
+``librp.so`` behind the C ABI of ``include/ragged_prefill.h``; this module only
+marshals torch tensors (device memory and the current stream) into that ABI.
+
+Entry points:
+  ragged_prefill(q, k, v, q_indptr, kv_indptr, ...)  one-shot (plans are cached)
+  Plan(q_indptr, kv_indptr, ...).run(q, k, v, ...)   plan once, run many
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+from . import _lib
+from ._lib import (RP_SPLIT_ALWAYS, RP_SPLIT_AUTO, RP_SPLIT_NEVER, RaggedPrefillError,
+                   RpPlanInfo, RpPlanOpts)
+
+__all__ = [
+    "available",
+    "ragged_prefill",
+    "Plan",
+    "RaggedPrefillError",
+    "RP_SPLIT_AUTO",
+    "RP_SPLIT_NEVER",
+    "RP_SPLIT_ALWAYS",
+    "ITEM_FIELDS",
+]
+
+# field names of one worklist item (int32 x 16), see rp_internal.h
+ITEM_FIELDS = ["q_tok0", "n_tok", "t0", "qo_len", "kv_row0", "kv_len", "kv_head", "key_begin",
+               "key_end", "slot", "request", "chunk", "cost", "lim_first", "reserved0",
+               "reserved1"]
+
+
+def available() -> bool:
+    """True if the library is built and the current HIP device is a gfx950."""
+    return bool(_lib.load().rp_available())
+
+
+def _host_indptr(x) -> np.ndarray:
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().to("cpu")  # device offsets are copied to the host (a sync)
+            return np.ascontiguousarray(x.numpy().astype(np.int32, copy=False))
+    except ImportError:  # pragma: no cover
+        pass
+    a = np.asarray(x)
+    if a.dtype.kind not in "iu":
+        raise TypeError("indptr must hold integers")
+    if a.size and (a.min() < np.iinfo(np.int32).min or a.max() > np.iinfo(np.int32).max):
+        raise ValueError("indptr does not fit int32")
+    return np.ascontiguousarray(a.astype(np.int32))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_tensor(t, name: str, rows_needed: int, heads: int, head_dim: int) -> None:
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU")
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16")
+    if t.dim() != 3 or t.shape[1] != heads or t.shape[2] != head_dim:
+        raise ValueError(f"{name} must have shape [rows, {heads}, {head_dim}], got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (packed NHD)")
+    if t.shape[0] < rows_needed:
+        raise ValueError(f"{name} has {t.shape[0]} rows but the offsets need {rows_needed}")
+
+
+def _default_scale(head_dim: int) -> float:
+    return float(np.float32(1.0 / math.sqrt(head_dim)))
+
+
+class Plan:
+    """A worklist for one batch shape: plan once, run many times.
+
+    ``kv_chunk`` (keys, multiple of 64; 0 = library default) fixes where long
+    KV is cut into partial states; ``split_mode`` only moves work between
+    workgroups and never changes results.  ``host_only`` plans can be
+    inspected (``items()``, ``info``) without a GPU.
+    """
+
+    def __init__(self, q_indptr, kv_indptr, num_qo_heads: int, num_kv_heads: int, head_dim: int,
+                 causal: bool = True, kv_chunk: int = 0, split_mode: int = RP_SPLIT_AUTO,
+                 host_only: bool = False):
+        lib = _lib.load()
+        self._lib = lib
+        self.q_indptr = _host_indptr(q_indptr)
+        self.kv_indptr = _host_indptr(kv_indptr)
+        if self.q_indptr.shape != self.kv_indptr.shape or self.q_indptr.ndim != 1 or self.q_indptr.size < 1:
+            raise ValueError("q_indptr and kv_indptr must be 1-D with the same length >= 1")
+        self.batch = int(self.q_indptr.size - 1)
+        self.num_qo_heads = int(num_qo_heads)
+        self.num_kv_heads = int(num_kv_heads)
+        self.head_dim = int(head_dim)
+        self.causal = bool(causal)
+        opts = RpPlanOpts(int(kv_chunk), int(split_mode), 1 if host_only else 0, 0)
+        handle = ctypes.c_void_p()
+        st = lib.rp_plan_create(_ptr(self.q_indptr), _ptr(self.kv_indptr), self.batch,
+                                self.num_qo_heads, self.num_kv_heads, self.head_dim,
+                                1 if self.causal else 0, ctypes.byref(opts), ctypes.byref(handle))
+        _lib.check(st, "rp_plan_create")
+        self._handle = handle
+        self._workspace = None
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        if self._handle is None:
+            raise RuntimeError("plan has been closed")
+        return self._handle
+
+    @property
+    def info(self) -> dict:
+        inf = RpPlanInfo()
+        _lib.check(self._lib.rp_plan_get_info(self.handle, ctypes.byref(inf)), "rp_plan_get_info")
+        return {name: getattr(inf, name) for name, _ in RpPlanInfo._fields_}
+
+    @property
+    def workspace_bytes(self) -> int:
+        return int(self._lib.rp_plan_workspace_bytes(self.handle))
+
+    def items(self) -> np.ndarray:
+        n = self.info["num_items"]
+        buf = np.zeros((n, _lib.RP_ITEM_INTS), dtype=np.int32)
+        got = self._lib.rp_plan_copy_items(self.handle, _ptr(buf), n)
+        if got < 0:
+            _lib.check(int(got), "rp_plan_copy_items")
+        return buf[:got]
+
+    def run(self, q, k, v, out=None, lse=None, sm_scale: Optional[float] = None,
+            return_lse: bool = True, workspace=None, stream=None):
+        import torch
+        rows_q = int(self.q_indptr[-1])
+        rows_kv = int(self.kv_indptr[-1])
+        _check_tensor(q, "q", rows_q, self.num_qo_heads, self.head_dim)
+        _check_tensor(k, "k", rows_kv, self.num_kv_heads, self.head_dim)
+        _check_tensor(v, "v", rows_kv, self.num_kv_heads, self.head_dim)
+        if out is None:
+            out = torch.empty_like(q)
+        else:
+            _check_tensor(out, "out", rows_q, self.num_qo_heads, self.head_dim)
+        if lse is None and return_lse:
+            lse = torch.empty((q.shape[0], self.num_qo_heads), dtype=torch.float32, device=q.device)
+        if lse is not None:
+            if (lse.dtype != torch.float32 or lse.device != q.device or not lse.is_contiguous()
+                    or tuple(lse.shape[1:]) != (self.num_qo_heads,) or lse.shape[0] < rows_q):
+                raise ValueError("lse must be a contiguous float32 [rows, num_qo_heads] GPU tensor")
+        need = self.workspace_bytes
+        if workspace is None and need > 0:
+            if self._workspace is None or self._workspace.numel() < need:
+                self._workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            workspace = self._workspace
+        ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        scale = _default_scale(self.head_dim) if sm_scale is None else float(sm_scale)
+        st = self._lib.rp_run(self.handle, ctypes.c_void_p(q.data_ptr()),
+                              ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+                              ctypes.c_void_p(out.data_ptr()),
+                              ctypes.c_void_p(lse.data_ptr()) if lse is not None else None,
+                              ctypes.c_float(scale), ws_ptr, ws_bytes, _stream_handle(stream))
+        _lib.check(st, "rp_run")
+        return out, lse
+
+    def close(self) -> None:
+        if self._handle is not None:
+            self._lib.rp_plan_destroy(self._handle)
+            self._handle = None
+            self._workspace = None
+
+    def __del__(self):  # pragma: no cover - best effort
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def ragged_prefill(q, k, v, q_indptr, kv_indptr, causal: bool = True,
+                   sm_scale: Optional[float] = None, out=None, lse=None,
+                   return_lse: bool = True, stream=None) -> Tuple[object, Optional[object]]:
+    """One-shot ragged prefill: returns (O, LSE or None).
+
+    q: bf16 [rows_q, Hq, D]; k, v: bf16 [rows_kv, Hkv, D] (contiguous, on the
+    GPU); q_indptr, kv_indptr: int [batch + 1] offsets (host or device; device
+    offsets are copied to the host).  sm_scale defaults to 1/sqrt(D).
+    """
+    import torch
+    lib = _lib.load()
+    qi = _host_indptr(q_indptr)
+    ki = _host_indptr(kv_indptr)
+    if qi.shape != ki.shape or qi.ndim != 1 or qi.size < 1:
+        raise ValueError("q_indptr and kv_indptr must be 1-D with the same length >= 1")
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q and k must be [rows, heads, head_dim]")
+    hq, d = int(q.shape[1]), int(q.shape[2])
+    hkv = int(k.shape[1])
+    batch = int(qi.size - 1)
+    _check_tensor(q, "q", int(qi[-1]), hq, d)
+    _check_tensor(k, "k", int(ki[-1]), hkv, d)
+    _check_tensor(v, "v", int(ki[-1]), hkv, d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor(out, "out", int(qi[-1]), hq, d)
+    if lse is None and return_lse:
+        lse = torch.empty((q.shape[0], hq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape[1:]) != (hq,) or lse.shape[0] < int(qi[-1])):
+        raise ValueError("lse must be a contiguous float32 [rows, num_qo_heads] GPU tensor")
+    scale = _default_scale(d) if sm_scale is None else float(sm_scale)
+    st = lib.ragged_prefill_bf16(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                                 ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                 ctypes.c_void_p(lse.data_ptr()) if lse is not None else None,
+                                 _ptr(qi), _ptr(ki), batch, hq, hkv, d, 1 if causal else 0,
+                                 ctypes.c_float(scale), _stream_handle(stream))
+    _lib.check(st, "ragged_prefill_bf16")
+    return out, lse

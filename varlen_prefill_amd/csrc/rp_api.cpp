@@ -1,0 +1,411 @@
+// C ABI of the ragged prefill attention library: validation, plan/run,
+// workspace management, status codes and logging.  Declared in
+// include/ragged_prefill.h, which states the contract of every entry point.
+#include "ragged_prefill.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <list>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "rp_internal.h"
+#include "rp_plan.h"
+
+struct rp_plan {
+    rp::HostPlan host;
+    int device = -1;
+    rp::Item *d_items = nullptr;
+    rp::MergeItem *d_merges = nullptr;
+    bool host_only = false;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const std::string &msg)
+{
+    g_last_error = msg;
+    return status;
+}
+
+// ---- logging: RP_LOGLEVEL (0 off, 1 plans, 3 launches), RP_LOGDEST (stderr, stdout or a path)
+int log_level()
+{
+    static int level = [] {
+        const char *s = std::getenv("RP_LOGLEVEL");
+        return s ? std::atoi(s) : 0;
+    }();
+    return level;
+}
+
+FILE *log_file()
+{
+    static FILE *f = [] {
+        const char *d = std::getenv("RP_LOGDEST");
+        if (d == nullptr || std::strcmp(d, "stderr") == 0)
+            return stderr;
+        if (std::strcmp(d, "stdout") == 0)
+            return stdout;
+        FILE *x = std::fopen(d, "a");
+        return x ? x : stderr;
+    }();
+    return f;
+}
+
+void logf(int level, const char *fmt, ...)
+{
+    if (log_level() < level)
+        return;
+    FILE *f = log_file();
+    std::fprintf(f, "[ragged_prefill] ");
+    va_list ap;
+    va_start(ap, fmt);
+    std::vfprintf(f, fmt, ap);
+    va_end(ap);
+    std::fprintf(f, "\n");
+    std::fflush(f);
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_fail(hipError_t e, const char *what)
+{
+    return fail(RP_EDEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+int upload_plan(rp_plan *p)
+{
+    hipError_t e = hipGetDevice(&p->device);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    if (!p->host.items.empty()) {
+        const size_t n = p->host.items.size() * sizeof(rp::Item);
+        e = hipMalloc(reinterpret_cast<void **>(&p->d_items), n);
+        if (e != hipSuccess)
+            return fail(RP_ENOMEM, std::string("hipMalloc(worklist): ") + hipGetErrorString(e));
+        e = hipMemcpy(p->d_items, p->host.items.data(), n, hipMemcpyHostToDevice);
+        if (e != hipSuccess)
+            return hip_fail(e, "hipMemcpy(worklist)");
+    }
+    if (!p->host.merges.empty()) {
+        const size_t n = p->host.merges.size() * sizeof(rp::MergeItem);
+        e = hipMalloc(reinterpret_cast<void **>(&p->d_merges), n);
+        if (e != hipSuccess)
+            return fail(RP_ENOMEM, std::string("hipMalloc(merge list): ") + hipGetErrorString(e));
+        e = hipMemcpy(p->d_merges, p->host.merges.data(), n, hipMemcpyHostToDevice);
+        if (e != hipSuccess)
+            return hip_fail(e, "hipMemcpy(merge list)");
+    }
+    return RP_OK;
+}
+
+void free_plan(rp_plan *p)
+{
+    if (p == nullptr)
+        return;
+    if (p->d_items)
+        (void)hipFree(p->d_items);
+    if (p->d_merges)
+        (void)hipFree(p->d_merges);
+    delete p;
+}
+
+int create_plan(const int32_t *q_indptr, const int32_t *kv_indptr, int batch, int num_qo_heads,
+                int num_kv_heads, int head_dim, int causal, const rp_plan_opts *opts,
+                rp_plan **out)
+{
+    if (out == nullptr)
+        return fail(RP_EINVAL, "out must not be NULL");
+    *out = nullptr;
+    rp::PlanShape shape;
+    shape.batch = batch;
+    shape.num_qo_heads = num_qo_heads;
+    shape.num_kv_heads = num_kv_heads;
+    shape.head_dim = head_dim;
+    shape.causal = causal ? 1 : 0;
+    shape.kv_chunk = opts ? opts->kv_chunk : 0;
+    shape.split_mode = opts ? opts->split_mode : 0;
+    rp_plan *p = new (std::nothrow) rp_plan;
+    if (p == nullptr)
+        return fail(RP_ENOMEM, "out of host memory");
+    std::string err;
+    int st;
+    try {
+        st = rp::build_plan(q_indptr, kv_indptr, shape, p->host, err);
+    } catch (const std::bad_alloc &) {
+        delete p;
+        return fail(RP_ENOMEM, "out of host memory while planning");
+    }
+    if (st != RP_OK) {
+        delete p;
+        return fail(st, err);
+    }
+    p->host_only = opts && opts->host_only;
+    if (!p->host_only) {
+        st = upload_plan(p);
+        if (st != RP_OK) {
+            free_plan(p);
+            return st;
+        }
+    }
+    logf(1, "plan: batch=%d Hq=%d Hkv=%d D=%d causal=%d total_q=%lld total_kv=%lld items=%zu "
+            "partial=%lld merges=%zu kv_chunk=%d gflop=%.3f mb=%.3f",
+         batch, num_qo_heads, num_kv_heads, head_dim, causal, (long long)p->host.total_q,
+         (long long)p->host.total_kv, p->host.items.size(), (long long)p->host.num_partial_items,
+         p->host.merges.size(), p->host.shape.kv_chunk, p->host.flops * 1e-9, p->host.bytes * 1e-6);
+    *out = p;
+    return RP_OK;
+}
+
+int run_plan(const rp_plan *p, const void *q, const void *k, const void *v, void *o, float *lse,
+             float sm_scale, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (p == nullptr)
+        return fail(RP_EINVAL, "plan must not be NULL");
+    if (p->host_only)
+        return fail(RP_EINVAL, "a host-only plan cannot be run");
+    if (!std::isfinite(sm_scale))
+        return fail(RP_EINVAL, "sm_scale must be finite");
+    const rp::HostPlan &h = p->host;
+    if (h.items.empty())
+        return RP_OK;  // empty batch / no query rows: nothing to launch
+    if (q == nullptr || o == nullptr)
+        return fail(RP_EINVAL, "q and o must not be NULL");
+    if (h.total_kv > 0 && (k == nullptr || v == nullptr))
+        return fail(RP_EINVAL, "k and v must not be NULL");
+    if (!aligned16(q) || !aligned16(o) || !aligned16(k) || !aligned16(v) ||
+        (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+        return fail(RP_EINVAL, "q, k, v and o must be 16-byte aligned (lse 4-byte)");
+    const size_t need = h.workspace_bytes();
+    if (need > 0) {
+        if (workspace == nullptr || workspace_bytes < need)
+            return fail(RP_EINVAL, "workspace too small: need " + std::to_string(need) + " bytes");
+        if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+            return fail(RP_EINVAL, "workspace must be 256-byte aligned");
+    }
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    if (dev != p->device)
+        return fail(RP_EINVAL, "plan was created on device " + std::to_string(p->device) +
+                                   " but device " + std::to_string(dev) + " is current");
+
+    float *part_o = static_cast<float *>(workspace);
+    float *part_lse = need ? reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                                       ((h.part_o_bytes() + 255) & ~size_t(255)))
+                           : nullptr;
+    rp::TileArgs ta{};
+    ta.q = q;
+    ta.k = k;
+    ta.v = v;
+    ta.o = o;
+    ta.lse = lse;
+    ta.part_o = part_o;
+    ta.part_lse = part_lse;
+    ta.items = p->d_items;
+    ta.num_qo_heads = h.shape.num_qo_heads;
+    ta.num_kv_heads = h.shape.num_kv_heads;
+    ta.group = h.shape.num_qo_heads / h.shape.num_kv_heads;
+    ta.causal = h.shape.causal;
+    ta.scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
+    logf(3, "launch tile kernel: D=%d items=%zu merges=%zu scale_log2=%g", h.shape.head_dim,
+         h.items.size(), h.merges.size(), (double)ta.scale_log2);
+    int st = rp::launch_tile_kernel(h.shape.head_dim, ta, (int64_t)h.items.size(), stream);
+    if (st != (int)hipSuccess)
+        return hip_fail((hipError_t)st, "tile kernel launch");
+    if (!h.merges.empty()) {
+        rp::MergeArgs ma{};
+        ma.o = o;
+        ma.lse = lse;
+        ma.part_o = part_o;
+        ma.part_lse = part_lse;
+        ma.items = p->d_merges;
+        ma.num_qo_heads = h.shape.num_qo_heads;
+        ma.group = ta.group;
+        st = rp::launch_merge_kernel(h.shape.head_dim, ma, (int64_t)h.merges.size(), stream);
+        if (st != (int)hipSuccess)
+            return hip_fail((hipError_t)st, "merge kernel launch");
+    }
+    return RP_OK;
+}
+
+// ---- one-shot path: per-device plan cache and library-owned workspace ----
+struct CachedPlan {
+    std::vector<int32_t> q_indptr, kv_indptr;
+    int num_qo_heads, num_kv_heads, head_dim, causal;
+    rp_plan *plan;
+};
+
+struct DeviceState {
+    std::list<CachedPlan> plans;  // most recent first
+    void *workspace = nullptr;
+    size_t workspace_bytes = 0;
+};
+
+constexpr size_t kPlanCacheSize = 8;
+std::mutex g_oneshot_mutex;
+std::vector<DeviceState> g_devices;
+
+}  // namespace
+
+extern "C" {
+
+const char *rp_status_string(int status)
+{
+    switch (status) {
+    case RP_OK: return "RP_OK";
+    case RP_EINVAL: return "RP_EINVAL: invalid argument";
+    case RP_EUNSUPPORTED: return "RP_EUNSUPPORTED: unsupported configuration";
+    case RP_ENOMEM: return "RP_ENOMEM: out of memory";
+    case RP_EDEVICE: return "RP_EDEVICE: HIP runtime or launch failure";
+    default: return "unknown status";
+    }
+}
+
+const char *rp_last_error(void) { return g_last_error.c_str(); }
+
+int rp_abi_version(void) { return RP_ABI_VERSION; }
+
+int rp_available(void)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 0;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return 0;
+    return std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+}
+
+int rp_plan_create(const int32_t *q_indptr, const int32_t *kv_indptr, int batch, int num_qo_heads,
+                   int num_kv_heads, int head_dim, int causal, const rp_plan_opts *opts,
+                   rp_plan **out)
+{
+    return create_plan(q_indptr, kv_indptr, batch, num_qo_heads, num_kv_heads, head_dim, causal,
+                       opts, out);
+}
+
+int rp_plan_get_info(const rp_plan *p, rp_plan_info *info)
+{
+    if (p == nullptr || info == nullptr)
+        return fail(RP_EINVAL, "plan and info must not be NULL");
+    const rp::HostPlan &h = p->host;
+    std::memset(info, 0, sizeof *info);
+    info->num_items = (int64_t)h.items.size();
+    info->num_partial_items = h.num_partial_items;
+    info->num_merge_items = (int64_t)h.merges.size();
+    info->total_q = h.total_q;
+    info->total_kv = h.total_kv;
+    info->tile_rows = rp::kTileRows;
+    info->tile_tokens = h.tile_tokens;
+    info->key_block = rp::key_block(h.shape.head_dim);
+    info->kv_chunk = h.shape.kv_chunk;
+    info->flops = h.flops;
+    info->bytes = h.bytes;
+    info->workspace_bytes = h.workspace_bytes();
+    return RP_OK;
+}
+
+size_t rp_plan_workspace_bytes(const rp_plan *p) { return p ? p->host.workspace_bytes() : 0; }
+
+int64_t rp_plan_copy_items(const rp_plan *p, int32_t *dst, int64_t capacity)
+{
+    if (p == nullptr || (dst == nullptr && capacity > 0) || capacity < 0)
+        return fail(RP_EINVAL, "bad arguments");
+    const int64_t n = std::min<int64_t>(capacity, (int64_t)p->host.items.size());
+    if (n > 0)
+        std::memcpy(dst, p->host.items.data(), (size_t)n * sizeof(rp::Item));
+    return n;
+}
+
+int rp_run(const rp_plan *p, const void *q, const void *k, const void *v, void *o, float *lse,
+           float sm_scale, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return run_plan(p, q, k, v, o, lse, sm_scale, workspace, workspace_bytes, stream);
+}
+
+void rp_plan_destroy(rp_plan *p) { free_plan(p); }
+
+int ragged_prefill_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
+                        const int32_t *q_indptr, const int32_t *kv_indptr, int batch,
+                        int num_qo_heads, int num_kv_heads, int head_dim, int causal,
+                        float sm_scale, void *stream)
+{
+    if (batch < 0)
+        return fail(RP_EINVAL, "batch must be >= 0");
+    if (batch == 0)
+        return RP_OK;  // empty batch: early return, no launch
+    if (q_indptr == nullptr || kv_indptr == nullptr)
+        return fail(RP_EINVAL, "q_indptr and kv_indptr must not be NULL");
+    if (!std::isfinite(sm_scale))
+        return fail(RP_EINVAL, "sm_scale must be finite");
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_oneshot_mutex);
+    if ((int)g_devices.size() <= dev)
+        g_devices.resize((size_t)dev + 1);
+    DeviceState &ds = g_devices[(size_t)dev];
+    const int cz = causal ? 1 : 0;
+    rp_plan *plan = nullptr;
+    for (auto it = ds.plans.begin(); it != ds.plans.end(); ++it) {
+        if (it->num_qo_heads == num_qo_heads && it->num_kv_heads == num_kv_heads &&
+            it->head_dim == head_dim && it->causal == cz &&
+            (int)it->q_indptr.size() == batch + 1 &&
+            std::memcmp(it->q_indptr.data(), q_indptr, sizeof(int32_t) * (batch + 1)) == 0 &&
+            std::memcmp(it->kv_indptr.data(), kv_indptr, sizeof(int32_t) * (batch + 1)) == 0) {
+            plan = it->plan;
+            ds.plans.splice(ds.plans.begin(), ds.plans, it);
+            break;
+        }
+    }
+    if (plan == nullptr) {
+        int st = create_plan(q_indptr, kv_indptr, batch, num_qo_heads, num_kv_heads, head_dim, cz,
+                             nullptr, &plan);
+        if (st != RP_OK)
+            return st;
+        CachedPlan cp;
+        cp.q_indptr.assign(q_indptr, q_indptr + batch + 1);
+        cp.kv_indptr.assign(kv_indptr, kv_indptr + batch + 1);
+        cp.num_qo_heads = num_qo_heads;
+        cp.num_kv_heads = num_kv_heads;
+        cp.head_dim = head_dim;
+        cp.causal = cz;
+        cp.plan = plan;
+        ds.plans.push_front(std::move(cp));
+        while (ds.plans.size() > kPlanCacheSize) {
+            // the evicted plan's worklist may still be read by queued work
+            (void)hipDeviceSynchronize();
+            free_plan(ds.plans.back().plan);
+            ds.plans.pop_back();
+        }
+    }
+    const size_t need = plan->host.workspace_bytes();
+    if (need > ds.workspace_bytes) {
+        if (ds.workspace) {
+            (void)hipDeviceSynchronize();  // queued work may still use the old workspace
+            (void)hipFree(ds.workspace);
+            ds.workspace = nullptr;
+            ds.workspace_bytes = 0;
+        }
+        e = hipMalloc(&ds.workspace, need);
+        if (e != hipSuccess) {
+            ds.workspace = nullptr;
+            return fail(RP_ENOMEM, std::string("hipMalloc(workspace): ") + hipGetErrorString(e));
+        }
+        ds.workspace_bytes = need;
+    }
+    return run_plan(plan, q, k, v, o, lse, sm_scale, ds.workspace, ds.workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,101 @@
+// Internal definitions shared by the host library and the gfx950 kernels.
+//
+// A plan is a list of tile work items.  A tile is a block of up to
+// kTileRows "rows" of one request and one kv head, where a row is a
+// (query token, qo head) pair: the g = num_qo_heads / num_kv_heads qo heads of a
+// GQA group that read the same kv head are packed together, token-major, so a
+// single K/V block in LDS serves all of them (GQA as on page "Module
+// flashinfer", functions: num_qo_heads a multiple of num_kv_heads).
+//
+// Each item covers a request-relative key range.  KV is cut into canonical
+// chunks of kv_chunk keys at request-relative offsets.  A tile whose visible
+// keys span several chunks is split: one item per chunk writes an fp32
+// partial state (o_c, lse_c) into the workspace and a merge item folds the
+// chunks left to right (the merge of attention states of page
+// "flashinfer-ai/flashinfer", "Merge Attention States").  Chunk boundaries
+// depend only on the request, never on the batch, so per-request results do
+// not change with batch composition.
+#pragma once
+
+#include <cstdint>
+
+namespace rp {
+
+constexpr int kTileRows = 128;      // rows per tile: 4 waves x 32 rows
+constexpr int kThreads = 256;       // threads per tile workgroup
+constexpr int kMergeThreads = 256;  // threads per merge workgroup
+constexpr int kDefaultKvChunk = 8192;
+constexpr int kChunkAlign = 64;     // kv_chunk must be a multiple of this
+// Key blocks are computed with P split into a bf16 hi part and a bf16 lo
+// remainder when the block is partially masked for the tile or when the
+// tile's first row sees at most this many keys.
+constexpr int kHiLoKeys = 128;
+
+inline constexpr int key_block(int head_dim) { return head_dim == 128 ? 64 : 32; }
+
+// Work item of the tile kernel: 16 int32 (64 bytes).
+struct Item {
+    int32_t q_tok0;     // global row (in Q/O) of the tile's first token
+    int32_t n_tok;      // tokens in the tile (>= 1)
+    int32_t t0;         // request-relative index of the first token
+    int32_t qo_len;     // request's query length
+    int32_t kv_row0;    // global row (in K/V) of the request's key 0
+    int32_t kv_len;     // request's key length
+    int32_t kv_head;    // kv head; qo heads kv_head*g .. kv_head*g+g-1
+    int32_t key_begin;  // request-relative first key of this item
+    int32_t key_end;    // request-relative end key (exclusive); <= key_begin: no keys
+    int32_t slot;       // -1: write final O/LSE; >= 0: partial-state slot
+    int32_t request;    // request index in the batch
+    int32_t chunk;      // canonical chunk index of a partial item; chunk count otherwise
+    int32_t cost;       // planner's cost estimate (key blocks, hi/lo weighted)
+    int32_t lim_first;  // keys visible to the tile's first row (causal limit)
+    int32_t reserved0;
+    int32_t reserved1;
+};
+static_assert(sizeof(Item) == 64, "Item must stay 16 int32");
+
+// Work item of the merge kernel: 8 int32.
+struct MergeItem {
+    int32_t q_tok0;
+    int32_t n_tok;
+    int32_t kv_head;
+    int32_t slot0;      // chunk c of this tile lives in slot slot0 + c
+    int32_t n_chunks;
+    int32_t request;
+    int32_t reserved0;
+    int32_t reserved1;
+};
+static_assert(sizeof(MergeItem) == 32, "MergeItem must stay 8 int32");
+
+// Kernel arguments (passed by value).
+struct TileArgs {
+    const void *q;
+    const void *k;
+    const void *v;
+    void *o;
+    float *lse;            // may be null
+    float *part_o;         // [slots][kTileRows][head_dim] fp32
+    float *part_lse;       // [slots][kTileRows] fp32, base-2 log-sum-exp
+    const Item *items;
+    int32_t num_qo_heads;
+    int32_t num_kv_heads;
+    int32_t group;         // num_qo_heads / num_kv_heads
+    int32_t causal;
+    float scale_log2;      // sm_scale * log2(e)
+};
+
+struct MergeArgs {
+    void *o;
+    float *lse;
+    const float *part_o;
+    const float *part_lse;
+    const MergeItem *items;
+    int32_t num_qo_heads;
+    int32_t group;
+};
+
+// Host-side launchers (defined in the .hip file).  Return a hipError_t value.
+int launch_tile_kernel(int head_dim, const TileArgs &args, int64_t num_items, void *stream);
+int launch_merge_kernel(int head_dim, const MergeArgs &args, int64_t num_items, void *stream);
+
+}  // namespace rp

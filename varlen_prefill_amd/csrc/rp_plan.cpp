@@ -1,0 +1,218 @@
+// Host planner: turns ragged offsets into a balanced tile worklist.
+//
+// Tiles: each request's query tokens are cut into tiles of kTileRows / g
+// tokens (g = GQA group size), one tile per (token range, kv head).  KV is cut
+// into canonical chunks of kv_chunk keys at request-relative offsets; a tile
+// whose visible keys reach past one chunk gets one work item per chunk, each
+// writing an fp32 partial state, and one merge item (split-KV, page "vllm-rlt
+// PR #112", results notes: split-KV parallelism pays off for few requests).
+// Items are ordered longest-first (LPT), so the hardware's in-order workgroup
+// dispatch approximates greedy longest-processing-time scheduling.
+//
+// The chunk grid is a property of the request alone, which keeps per-request
+// results independent of the batch ("balanced tile worklist" with automatic
+// split-KV, page "flashinfer-ai/flashinfer", attention API, task-scheduled
+// attention).
+#include "rp_plan.h"
+
+#include <algorithm>
+#include <numeric>
+
+namespace rp {
+
+namespace {
+
+constexpr int kOk = 0;
+constexpr int kEInval = -1;
+constexpr int kEUnsupported = -2;
+
+int64_t limit_of(int64_t i, int64_t qo_len, int64_t kv_len, bool causal)
+{
+    if (!causal)
+        return kv_len;
+    int64_t lim = i + kv_len - qo_len + 1;
+    return lim < 0 ? 0 : (lim > kv_len ? kv_len : lim);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+int64_t visible_keys(int64_t i, int64_t qo_len, int64_t kv_len, bool causal)
+{
+    return limit_of(i, qo_len, kv_len, causal);
+}
+
+size_t HostPlan::part_o_bytes() const
+{
+    return (size_t)num_slots * kTileRows * (size_t)shape.head_dim * sizeof(float);
+}
+
+size_t HostPlan::workspace_bytes() const
+{
+    if (num_slots == 0)
+        return 0;
+    return align256(part_o_bytes()) + align256((size_t)num_slots * kTileRows * sizeof(float));
+}
+
+int build_plan(const int32_t *q_indptr, const int32_t *kv_indptr, const PlanShape &shape_in,
+               HostPlan &out, std::string &err)
+{
+    PlanShape shape = shape_in;
+    if (shape.kv_chunk == 0)
+        shape.kv_chunk = kDefaultKvChunk;
+    if (shape.batch < 0) {
+        err = "batch must be >= 0";
+        return kEInval;
+    }
+    if (shape.num_qo_heads <= 0 || shape.num_kv_heads <= 0) {
+        err = "head counts must be positive";
+        return kEInval;
+    }
+    if (shape.num_qo_heads % shape.num_kv_heads != 0) {
+        err = "num_qo_heads must be a multiple of num_kv_heads";
+        return kEInval;
+    }
+    const int group = shape.num_qo_heads / shape.num_kv_heads;
+    if (group > kTileRows) {
+        err = "GQA group size (num_qo_heads / num_kv_heads) above 128 is not supported";
+        return kEUnsupported;
+    }
+    if (shape.head_dim != 128 && shape.head_dim != 256) {
+        err = "head_dim must be 128 or 256";
+        return kEUnsupported;
+    }
+    if (shape.causal != 0 && shape.causal != 1) {
+        err = "causal must be 0 or 1";
+        return kEInval;
+    }
+    if (shape.kv_chunk < kChunkAlign || shape.kv_chunk % kChunkAlign != 0) {
+        err = "kv_chunk must be a positive multiple of 64";
+        return kEInval;
+    }
+    if (shape.split_mode < 0 || shape.split_mode > 2) {
+        err = "unknown split_mode";
+        return kEInval;
+    }
+    if (shape.split_mode == 1) {
+        err = "split_mode NEVER (in-workgroup chunk folding) is not implemented";
+        return kEUnsupported;
+    }
+    if (shape.batch > 0 && (q_indptr == nullptr || kv_indptr == nullptr)) {
+        err = "q_indptr and kv_indptr must not be NULL when batch > 0";
+        return kEInval;
+    }
+    if (shape.batch > 0 && (q_indptr[0] < 0 || kv_indptr[0] < 0)) {
+        err = "indptr entries must be >= 0";
+        return kEInval;
+    }
+    for (int b = 0; b < shape.batch; ++b) {
+        if (q_indptr[b + 1] < q_indptr[b] || kv_indptr[b + 1] < kv_indptr[b]) {
+            err = "indptr must be non-decreasing (request " + std::to_string(b) + ")";
+            return kEInval;
+        }
+    }
+
+    HostPlan plan;
+    plan.shape = shape;
+    plan.tile_tokens = kTileRows / group;
+    const int bk = key_block(shape.head_dim);
+    const bool causal = shape.causal != 0;
+    const int64_t C = shape.kv_chunk;
+
+    if (shape.batch > 0) {
+        plan.max_q_row = q_indptr[shape.batch];
+        plan.max_kv_row = kv_indptr[shape.batch];
+        plan.total_q = (int64_t)q_indptr[shape.batch] - q_indptr[0];
+        plan.total_kv = (int64_t)kv_indptr[shape.batch] - kv_indptr[0];
+    }
+
+    double pairs_total = 0.0;
+    for (int b = 0; b < shape.batch; ++b) {
+        const int64_t qo = (int64_t)q_indptr[b + 1] - q_indptr[b];
+        const int64_t kv = (int64_t)kv_indptr[b + 1] - kv_indptr[b];
+        for (int64_t i = 0; i < qo; ++i)
+            pairs_total += (double)limit_of(i, qo, kv, causal);
+        if (qo == 0)
+            continue;
+        for (int64_t t0 = 0; t0 < qo; t0 += plan.tile_tokens) {
+            const int64_t n_tok = std::min<int64_t>(plan.tile_tokens, qo - t0);
+            const int64_t lim_first = limit_of(t0, qo, kv, causal);
+            const int64_t lim_last = limit_of(t0 + n_tok - 1, qo, kv, causal);
+            const int64_t key_end = lim_last;
+            const int64_t n_chunks = key_end > 0 ? (key_end + C - 1) / C : 0;
+            const bool split = n_chunks > 1;  // AUTO and ALWAYS: split every multi-chunk tile
+            for (int kvh = 0; kvh < shape.num_kv_heads; ++kvh) {
+                Item it{};
+                it.q_tok0 = (int32_t)(q_indptr[b] + t0);
+                it.n_tok = (int32_t)n_tok;
+                it.t0 = (int32_t)t0;
+                it.qo_len = (int32_t)qo;
+                it.kv_row0 = kv_indptr[b];
+                it.kv_len = (int32_t)kv;
+                it.kv_head = kvh;
+                it.request = b;
+                it.lim_first = (int32_t)lim_first;
+                if (!split) {
+                    it.key_begin = 0;
+                    it.key_end = (int32_t)key_end;
+                    it.slot = -1;
+                    it.chunk = (int32_t)n_chunks;
+                    plan.items.push_back(it);
+                } else {
+                    const int64_t slot0 = plan.num_slots;
+                    plan.num_slots += n_chunks;
+                    for (int64_t ch = 0; ch < n_chunks; ++ch) {
+                        Item pi = it;
+                        pi.key_begin = (int32_t)(ch * C);
+                        pi.key_end = (int32_t)std::min<int64_t>((ch + 1) * C, key_end);
+                        pi.slot = (int32_t)(slot0 + ch);
+                        pi.chunk = (int32_t)ch;
+                        plan.items.push_back(pi);
+                        ++plan.num_partial_items;
+                    }
+                    MergeItem mi{};
+                    mi.q_tok0 = it.q_tok0;
+                    mi.n_tok = it.n_tok;
+                    mi.kv_head = kvh;
+                    mi.slot0 = (int32_t)slot0;
+                    mi.n_chunks = (int32_t)n_chunks;
+                    mi.request = b;
+                    plan.merges.push_back(mi);
+                }
+            }
+        }
+    }
+    if (plan.num_slots > (int64_t)INT32_MAX / kTileRows) {
+        err = "too many partial states";
+        return kEUnsupported;
+    }
+
+    // cost: two MFMA halves per key block, one more on hi/lo blocks, plus a
+    // fixed epilogue share
+    for (Item &it : plan.items) {
+        int64_t cost = 4;
+        if (it.key_end > it.key_begin) {
+            const int64_t kb0 = it.key_begin / bk;
+            const int64_t kb1 = (it.key_end + bk - 1) / bk;
+            for (int64_t kb = kb0; kb < kb1; ++kb) {
+                const bool mask = (kb + 1) * bk > it.lim_first;
+                const bool hilo = mask || it.lim_first <= kHiLoKeys;
+                cost += hilo ? 3 : 2;
+            }
+        }
+        it.cost = (int32_t)std::min<int64_t>(cost, INT32_MAX);
+    }
+    std::stable_sort(plan.items.begin(), plan.items.end(),
+                     [](const Item &x, const Item &y) { return x.cost > y.cost; });
+
+    const double hd = shape.head_dim;
+    plan.flops = 4.0 * hd * shape.num_qo_heads * pairs_total;
+    plan.bytes = 2.0 * hd * (2.0 * shape.num_qo_heads * (double)plan.total_q +
+                             2.0 * shape.num_kv_heads * (double)plan.total_kv) +
+                 4.0 * shape.num_qo_heads * (double)plan.total_q;
+    out = std::move(plan);
+    return kOk;
+}
+
+}  // namespace rp
