@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Benchmark of ragged (varlen) batched prefill attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one call of the library's one-shot C entry point
+``ragged_prefill_bf16`` on a synthetic ragged batch already resident in HBM:
+argument validation, the plan lookup (the plan is built on the first call and
+cached per offsets/shape, i.e. planned once per batch as in the plan/run
+design), the tile kernel and, when the plan splits KV, the merge kernel.
+Prints ONE JSON line.
+
+Default workload: 8 requests, qo_len = kv_len ~ U[128, 2048] (recorded lengths),
+32 qo / 8 kv heads, head_dim 128, causal, bf16 N(0,1) inputs.
+
+Other modes:
+  --copy-probe-mib M   run a plain device copy of M MiB (read M, write M) a few
+                       times; used to scale rocprofv3 FETCH_SIZE/WRITE_SIZE.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ragged causal prefill TFLOP/s & tok/s (bf16 GQA hd128) + % of MFMA peak"
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E (published)
+KERNEL_SRC = os.path.join(ROOT, "varlen_prefill_amd", "csrc", "rp_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{kernel}_{workload}.json")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="hd128_gqa_causal")
+    p.add_argument("--noncausal", action="store_true", help="run the workload without the causal mask")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time of the oracle baseline sample")
+    p.add_argument("--copy-probe-mib", type=int, default=0)
+    return p.parse_args()
+
+
+def copy_probe(mib: int) -> None:
+    import torch
+    n = mib * (1 << 20)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 5}))
+
+
+def cpu_baseline(batch, cfg, causal: bool, sm_scale: float, target_s: float) -> dict:
+    """Time the fp64 oracle (as it stands) on a random sample of (token, head)
+    rows of the same workload, on all host cores."""
+    import oracle
+    rng = np.random.default_rng(2024)
+    total = int(batch.q_indptr[-1])
+    # request of each token and its visible key count
+    req = np.searchsorted(batch.q_indptr, np.arange(total), side="right") - 1
+    qo = np.diff(batch.q_indptr)[req].astype(np.int64)
+    kv = np.diff(batch.kv_indptr)[req].astype(np.int64)
+    i = np.arange(total) - batch.q_indptr[req]
+    lim = np.clip(i + kv - qo + 1, 0, kv) if causal else kv
+
+    def run(n):
+        toks = rng.integers(0, total, n)
+        heads = rng.integers(0, cfg.num_qo_heads, n)
+        t0 = time.perf_counter()
+        oracle.ragged_attention_rows(batch.q, batch.k, batch.v, batch.q_indptr, batch.kv_indptr,
+                                     cfg.num_qo_heads, cfg.num_kv_heads, causal, sm_scale, toks, heads)
+        dt = time.perf_counter() - t0
+        flops = float(np.sum(4.0 * cfg.head_dim * lim[toks]))
+        return n, dt, flops
+
+    n, dt, _ = run(256)                       # calibration
+    n_target = int(max(256, min(2_000_000, n * target_s / max(dt, 1e-3))))
+    n, dt, flops = run(n_target)
+    tflops = flops / dt / 1e12
+    flops_per_token = 4.0 * cfg.head_dim * cfg.num_qo_heads * float(np.mean(lim))
+    return {
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{n} random (token, qo head) rows of the same batch, {flops / 1e9:.1f} GFLOP, "
+                  f"{dt:.1f} s",
+        "tokens_per_s": tflops * 1e12 / flops_per_token,
+        "seconds": dt,
+    }
+
+
+def load_traffic(kernel: str, workload: str):
+    path = TRAFFIC_FILE.format(kernel=kernel, workload=workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None  # counters were taken on another version of the kernel
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(this path runs on a single GPU; see DESIGN.md for how it would shard)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+        return
+    import varlen_prefill_amd as vp
+    from varlen_prefill_amd import _lib
+    from workloads import get_config, make_config_batch
+
+    cfg = get_config(args.workload)
+    causal = cfg.causal and not args.noncausal
+    batch = make_config_batch(cfg)
+    sm_scale = float(np.float32(1.0 / math.sqrt(cfg.head_dim)))
+    dev = torch.device("cuda:0")
+    q, k, v = batch.q.to(dev), batch.k.to(dev), batch.v.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((q.shape[0], cfg.num_qo_heads), dtype=torch.float32, device=dev)
+    if not vp.available():
+        raise SystemExit("the gfx950 library is not usable on this device")
+
+    # plan statistics and host plan time (a fresh plan + worklist upload)
+    plan_times = []
+    for _ in range(5):
+        t0 = time.perf_counter()
+        plan = vp.Plan(batch.q_indptr, batch.kv_indptr, cfg.num_qo_heads, cfg.num_kv_heads,
+                       cfg.head_dim, causal)
+        plan_times.append(time.perf_counter() - t0)
+        info = plan.info
+        plan.close()
+    flops = info["flops"]
+    alg_bytes = info["bytes"]
+    launches = 1 + (1 if info["num_merge_items"] > 0 else 0)
+
+    lib = _lib.load()
+    stream = torch.cuda.current_stream()
+    qi = np.ascontiguousarray(batch.q_indptr, dtype=np.int32)
+    ki = np.ascontiguousarray(batch.kv_indptr, dtype=np.int32)
+    call_args = (ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                 ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(o.data_ptr()),
+                 ctypes.c_void_p(lse.data_ptr()), qi.ctypes.data_as(ctypes.c_void_p),
+                 ki.ctypes.data_as(ctypes.c_void_p), cfg.batch, cfg.num_qo_heads,
+                 cfg.num_kv_heads, cfg.head_dim, 1 if causal else 0, ctypes.c_float(sm_scale),
+                 ctypes.c_void_p(stream.cuda_stream))
+    step = lib.ragged_prefill_bf16
+
+    for _ in range(args.warmup):
+        _lib.check(step(*call_args), "ragged_prefill_bf16")
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        st = step(*call_args)
+        if st != 0:
+            _lib.check(st, "ragged_prefill_bf16")
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_s = t1 - t0
+    event_ms = ev0.elapsed_time(ev1)
+    ms_per_step = wall_s * 1e3 / args.steps
+    gpu_ms_per_step = event_ms / args.steps
+
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (gpu_ms_per_step * 1e-3) / 1e12
+    kernel = f"tile_kernel_hd{cfg.head_dim}"
+    traffic = load_traffic(kernel, cfg.name + ("" if causal else "_noncausal"))
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.name + ("" if causal else "_noncausal"),
+            "requests": cfg.batch,
+            "num_qo_heads": cfg.num_qo_heads,
+            "num_kv_heads": cfg.num_kv_heads,
+            "head_dim": cfg.head_dim,
+            "causal": causal,
+            "total_q": cfg.total_q,
+            "total_kv": cfg.total_kv,
+            "seed": cfg.seed,
+        },
+        "tokens_per_s": cfg.total_q / (ms_per_step * 1e-3),
+        "mfma_peak_frac": value / MFMA_BF16_PEAK_TFLOPS,
+        "alg_gflop_per_step": flops / 1e9,
+        "alg_mb_per_step": alg_bytes / 1e6,
+        "gpu_ms_per_step": gpu_ms_per_step,
+        "launches_per_step": launches,
+        "plan_ms_median": float(np.median(plan_times) * 1e3),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+            "traffic": traffic,
+            "kernel": kernel if launches == 1 else f"{kernel} + merge_kernel",
+            "alg_hbm_gbs": alg_bytes / (gpu_ms_per_step * 1e-3) / 1e9,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(batch, cfg, causal, sm_scale, args.cpu_seconds)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

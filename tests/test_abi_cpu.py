@@ -1,0 +1,112 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+The library loads, exports every function include/ragged_prefill.h declares,
+and its host logic (validation, planning, status codes, empty-batch early
+return) behaves as the header states.  No kernel is launched.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import varlen_prefill_amd as vp
+from varlen_prefill_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if not fn.endswith(".h"):
+            continue
+        text = open(os.path.join(ROOT, "include", fn)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w \*]*?\b(\w+)\s*\([^;{]*\)\s*;", text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    declared = _declared_functions()
+    assert declared == set(_lib.EXPORTS), declared ^ set(_lib.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = declared - exported
+    assert not missing, missing
+    for name in declared:
+        assert hasattr(lib, name)
+
+
+def test_version_and_status_strings():
+    lib = _lib.load()
+    assert lib.rp_abi_version() == 1
+    for st in (0, -1, -2, -3, -4):
+        assert lib.rp_status_string(st)
+    assert lib.rp_status_string(12345) == b"unknown status"
+
+
+def test_not_available_without_gpu():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert vp.available() is False
+
+
+def _plan(qi, ki, hq=8, hkv=2, d=128, causal=True, **kw):
+    return vp.Plan(qi, ki, hq, hkv, d, causal, host_only=True, **kw)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(hq=8, hkv=3), _lib.RP_EINVAL),              # Hq % Hkv != 0
+    (dict(d=64), _lib.RP_EUNSUPPORTED),               # head_dim
+    (dict(hq=0, hkv=1), _lib.RP_EINVAL),              # no heads
+    (dict(hq=256, hkv=1), _lib.RP_EUNSUPPORTED),      # group above 128
+    (dict(kv_chunk=100), _lib.RP_EINVAL),             # chunk not a multiple of 64
+    (dict(split_mode=7), _lib.RP_EINVAL),
+])
+def test_plan_validation(kwargs, status):
+    with pytest.raises(vp.RaggedPrefillError) as ei:
+        _plan([0, 5], [0, 5], **kwargs)
+    assert ei.value.status == status
+    assert _lib.load().rp_last_error()
+
+
+def test_plan_rejects_bad_offsets():
+    for qi, ki in (([0, 5, 3], [0, 5, 9]), ([0, 5, 9], [0, 5, 4]), ([-2, 5], [0, 5])):
+        with pytest.raises(vp.RaggedPrefillError) as ei:
+            _plan(qi, ki)
+        assert ei.value.status == _lib.RP_EINVAL
+
+
+def test_empty_batches_plan_to_nothing():
+    p = _plan([0], [0])
+    assert p.info["num_items"] == 0 and p.workspace_bytes == 0
+    p = _plan([4, 4, 4], [0, 10, 20])
+    assert p.info["num_items"] == 0 and p.info["total_q"] == 0
+
+
+def test_one_shot_empty_batch_returns_ok_without_device():
+    lib = _lib.load()
+    st = lib.ragged_prefill_bf16(None, None, None, None, None, None, None, 0, 8, 2, 128, 1,
+                                 ctypes.c_float(0.1), None)
+    assert st == _lib.RP_OK
+    st = lib.ragged_prefill_bf16(None, None, None, None, None, None, None, -1, 8, 2, 128, 1,
+                                 ctypes.c_float(0.1), None)
+    assert st == _lib.RP_EINVAL
+
+
+def test_run_rejects_host_only_plan():
+    lib = _lib.load()
+    p = _plan([0, 5], [0, 5])
+    st = lib.rp_run(p.handle, None, None, None, None, None, ctypes.c_float(0.1), None, 0, None)
+    assert st == _lib.RP_EINVAL
+    assert b"host-only" in lib.rp_last_error()
+    st = lib.rp_run(None, None, None, None, None, None, ctypes.c_float(0.1), None, 0, None)
+    assert st == _lib.RP_EINVAL

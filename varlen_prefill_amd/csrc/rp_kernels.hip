@@ -27,6 +27,7 @@
 
 #include <climits>
 #include <cstdint>
+#include <type_traits>
 
 #include "rp_internal.h"
 
@@ -41,6 +42,8 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kLn2 = 0.693147180559945309f;
+// lazy-rescale threshold in log2 units
+constexpr float kRescaleLog2 = 8.0f;
 
 template <int HD>
 struct Tile {
@@ -48,15 +51,22 @@ struct Tile {
     static constexpr int NB = BK / 32;           // 32-key MFMA row blocks of S^T
     static constexpr int DS = HD / 16;           // k-steps of the QK^T MFMA
     static constexpr int DB = HD / 32;           // 32-wide d blocks of O^T
-    static constexpr int KST = HD + 8;           // LDS row stride of K (bf16): 8-row phases hit distinct banks
-    static constexpr int VST = HD + 16;          // LDS row stride of V (bf16): 4-row transpose reads hit distinct banks
-    static constexpr int KTILE = BK * KST;
-    static constexpr int VTILE = BK * VST;
-    static constexpr int CPR = HD / 8;           // 16-byte chunks per K/V row
-    static constexpr int NLOAD = BK * CPR / kThreads;
-    static constexpr int LDS_BYTES = 2 * (KTILE + VTILE) * 2;
-    static_assert(NLOAD * kThreads == BK * CPR, "block must split evenly over threads");
+    static constexpr int RB = HD * 2;            // bytes per K/V row in LDS (unpadded)
+    static constexpr int CPR = HD / 8;           // 16-byte chunks per row
+    static constexpr int TILE_BYTES = BK * RB;   // one K (or V) block
+    static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
+    static constexpr int LDS_BYTES = 2 * STAGE_BYTES;  // double-buffered K and V
+    // direct-to-LDS loads: one instruction moves 64 lanes x 16 bytes
+    static constexpr int NLOAD = TILE_BYTES / (64 * 16) / (kThreads / 64);
+    static_assert(NLOAD * 64 * 16 * (kThreads / 64) == TILE_BYTES, "block must split evenly over waves");
 };
+
+// LDS layout: chunk c (16 bytes) of key row r sits at chunk position
+// c ^ swz(r) of that row.  K rows are read 8 rows at a time at one chunk
+// (swizzle r & 7); V rows 4 at a time over two adjacent chunks by the
+// transpose read (swizzle 2 (r & 3)).  Both patterns then touch distinct banks.
+__device__ inline int swz_k(int r) { return r & 7; }
+__device__ inline int swz_v(int r) { return (r & 3) << 1; }
 
 __device__ inline float pair_max(float x)
 {
@@ -99,8 +109,160 @@ __device__ inline void fold_state(float &lse_a, float (&o_a)[N], float lse_b, co
     lse_a = mx + log2f(s);
 }
 
+// Registers one wave carries through a tile.
+template <int HD>
+struct WaveState {
+    bf16x8 qf[Tile<HD>::DS];   // Q fragments (B operand of S^T = K Q^T)
+    f32x16 acc[Tile<HD>::DB];  // O^T accumulators
+    float m;                   // running max of scaled scores (log2 units)
+    float l;                   // this lane's part of the running sum
+};
+
+// One key block of one wave: S^T = K Q^T, mask, online softmax update,
+// O^T += V^T P^T.  MASK: the block holds keys beyond some row's causal limit
+// (the diagonal or the KV tail); thr is this lane's visible-key bound
+// relative to the block start and lane half.  HILO: P enters the PV product
+// as a bf16 hi part plus a bf16 lo remainder.  Each variant is straight-line
+// code so that LDS reads, MFMAs and VALU work can be interleaved.
+template <int HD, bool POS_SCALE, bool MASK, bool HILO>
+__device__ __attribute__((always_inline)) inline void block_step(
+    WaveState<HD> &st, const char *Ks, const char *Vs, float c, int thr, int qc, int h,
+    int grp, int s16)
+{
+    using T = Tile<HD>;
+    f32x16 s[T::NB];
+#pragma unroll
+    for (int n = 0; n < T::NB; ++n)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            s[n][j] = 0.0f;
+#pragma unroll
+    for (int ds = 0; ds < T::DS; ++ds) {
+#pragma unroll
+        for (int n = 0; n < T::NB; ++n) {
+            const int row = 32 * n + qc;
+            const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(
+                Ks + row * T::RB + 16 * ((2 * ds + h) ^ swz_k(row)));
+            s[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, st.qf[ds], s[n], 0, 0, 0);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // S^T register j of row block n holds key 32 n + 8 (j / 4) + 4 h + j % 4
+    float mx = -INFINITY;
+    if (POS_SCALE) {
+#pragma unroll
+        for (int n = 0; n < T::NB; ++n)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                if (MASK && 32 * n + 8 * (j >> 2) + (j & 3) >= thr)
+                    s[n][j] = -INFINITY;
+                mx = fmaxf(mx, s[n][j]);
+            }
+        mx = pair_max(mx) * c;
+    } else {
+#pragma unroll
+        for (int n = 0; n < T::NB; ++n)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                float x = s[n][j] * c;
+                if (MASK && 32 * n + 8 * (j >> 2) + (j & 3) >= thr)
+                    x = -INFINITY;
+                s[n][j] = x;
+                mx = fmaxf(mx, x);
+            }
+        mx = pair_max(mx);
+    }
+    // Lazy rescaling: the reference max only moves when the block max
+    // exceeds it by more than 2^8 (p <= 256 stays exact enough in bf16 and
+    // fp32); O, l and the LSE are all taken relative to the same reference,
+    // so the result does not depend on when it moves.
+    const bool grow = mx > st.m + kRescaleLog2;
+    const float m_ref = grow ? mx : st.m;
+    const float m_use = m_ref == -INFINITY ? 0.0f : m_ref;
+    float p[T::NB][16];
+#pragma unroll
+    for (int n = 0; n < T::NB; ++n)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const float x = POS_SCALE ? __builtin_fmaf(s[n][j], c, -m_use) : s[n][j] - m_use;
+            p[n][j] = fast_exp2(x);
+        }
+    // row-sum part of this lane: fixed pairwise tree
+    float t8[T::NB * 8];
+#pragma unroll
+    for (int n = 0; n < T::NB; ++n)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            t8[n * 8 + j] = p[n][2 * j] + p[n][2 * j + 1];
+#pragma unroll
+    for (int w = T::NB * 4; w >= 1; w >>= 1)
+#pragma unroll
+        for (int j = 0; j < w; ++j)
+            t8[j] = t8[2 * j] + t8[2 * j + 1];
+    const float psum = t8[0];
+    if (__any(grow)) {
+        const float alpha = fast_exp2(st.m - m_use);   // 1 where the reference stays, 0 at the start
+        st.l *= alpha;
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                st.acc[db][j] *= alpha;
+    }
+    st.l += psum;
+    st.m = m_ref;
+
+    // P as the B operand of O^T += V^T P^T: k-step t of row block n takes,
+    // in lane half h, element e = key 32 n + 16 t + 4 h + 8 (e / 4) + e % 4,
+    // i.e. this lane's S^T registers j = 8 t + e.
+    bf16x8 ph[T::NB][2];
+    bf16x8 pl[T::NB][2];
+#pragma unroll
+    for (int n = 0; n < T::NB; ++n)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float pv = p[n][8 * t + e];
+                const __bf16 hb = (__bf16)pv;
+                ph[n][t][e] = hb;
+                if (HILO)
+                    pl[n][t][e] = (__bf16)(pv - (float)hb);
+            }
+
+    __builtin_amdgcn_sched_barrier(0);
+    // A operand: lane (h, d = 32 db + lane % 32) needs V[key][d] for the 8
+    // keys above; each LDS transpose read delivers 4 consecutive keys.
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db) {
+#pragma unroll
+        for (int n = 0; n < T::NB; ++n) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                // source lane s16 of each 16-lane group reads key row
+                // 32 n + 16 t + 4 h + s16 / 4 (and 8 rows further), d = 32 db +
+                // 16 (grp & 1) + 4 (s16 & 3): chunk c, byte 8 (s16 & 1) within it
+                const int row = 32 * n + 16 * t + 4 * h + (s16 >> 2);
+                const int cc = 4 * db + 2 * (grp & 1) + ((s16 & 3) >> 1);
+                const char *vp = Vs + row * T::RB + 16 * (cc ^ swz_v(row)) + 8 * (s16 & 1);
+                const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4 *)((__attribute__((address_space(3))) char *)vp));
+                const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4 *)((__attribute__((address_space(3))) char *)(vp + 8 * T::RB)));
+                // join the two 4-key halves as one 16-byte vector (element-wise
+                // inserts into a bf16 vector are not lowered reliably)
+                const i16x8 v01 = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, v01);
+                st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, ph[n][t], st.acc[db], 0, 0, 0);
+                if (HILO)
+                    st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl[n][t], st.acc[db], 0, 0, 0);
+            }
+        }
+    }
+}
+
 template <int HD, bool POS_SCALE>
-__device__ inline void tile_body(const TileArgs &a, const Item &it, __bf16 *smem)
+__device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
 {
     using T = Tile<HD>;
     const int tid = threadIdx.x;
@@ -108,6 +270,8 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, __bf16 *smem
     const int w = tid >> 6;
     const int h = lane >> 5;          // which half of the wave
     const int qc = lane & 31;         // MFMA column = the wave's row
+    const int grp = lane >> 4;
+    const int s16 = lane & 15;
     const int g = a.group;
     const int r = w * 32 + qc;        // tile row
     const int tok = r / g;
@@ -123,221 +287,109 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, __bf16 *smem
         lim_row = lr < 0 ? 0 : (lr > it.kv_len ? it.kv_len : lr);
     }
 
-    // Q fragments: B operand of S^T = K Q^T; lane holds Q[row][16 ds + 8 h .. +7]
-    bf16x8 qf[T::DS];
+    WaveState<HD> st;
     {
         const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(
             static_cast<const __bf16 *>(a.q) + q_row * HD + 8 * h);
 #pragma unroll
         for (int ds = 0; ds < T::DS; ++ds) {
             if (row_valid) {
-                qf[ds] = qp[2 * ds];
+                st.qf[ds] = qp[2 * ds];
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    qf[ds][e] = (__bf16)0.0f;
+                    st.qf[ds][e] = (__bf16)0.0f;
             }
         }
     }
-
-    f32x16 acc[T::DB];
 #pragma unroll
     for (int db = 0; db < T::DB; ++db)
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-            acc[db][j] = 0.0f;
-    float m = -INFINITY;   // running max of scaled scores (log2 units)
-    float l = 0.0f;        // this lane's part of the running sum
+            st.acc[db][j] = 0.0f;
+    st.m = -INFINITY;
+    st.l = 0.0f;
 
     const float c = a.scale_log2;
     const int kb_begin = it.key_begin / T::BK;
     const int kb_end = it.key_end > it.key_begin ? (it.key_end + T::BK - 1) / T::BK : kb_begin;
     const bool hilo_all = it.lim_first <= kHiLoKeys;
 
-    const size_t kv_stride = (size_t)a.num_kv_heads * HD;
-    const __bf16 *kbase = static_cast<const __bf16 *>(a.k) +
-                          ((size_t)it.kv_row0 * a.num_kv_heads + it.kv_head) * HD;
-    const __bf16 *vbase = static_cast<const __bf16 *>(a.v) +
-                          ((size_t)it.kv_row0 * a.num_kv_heads + it.kv_head) * HD;
+    const size_t head_off = ((size_t)it.kv_row0 * a.num_kv_heads + it.kv_head) * HD;
+    const __bf16 *kbase = static_cast<const __bf16 *>(a.k) + head_off;
+    const __bf16 *vbase = static_cast<const __bf16 *>(a.v) + head_off;
 
-    uint4 kst[T::NLOAD], vst[T::NLOAD];
-    auto gload = [&](int kb) {
+    // Staging: direct-to-LDS loads.  Wave w, load i fills LDS chunks
+    // (4 w + i) * 64 + lane of the tile: key row r = chunk / CPR, position
+    // p = chunk % CPR, which holds global chunk p ^ swz(r).  Rows past the end
+    // of the request are clamped to its last key: those keys are masked
+    // (P = 0 exactly), so the data there is inert.
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    int grow_[T::NLOAD], kcol[T::NLOAD], vcol[T::NLOAD];
 #pragma unroll
-        for (int i = 0; i < T::NLOAD; ++i) {
-            const int ci = tid + i * kThreads;
-            const int key = ci / T::CPR;
-            const int cc = ci - key * T::CPR;
-            const int kk = kb * T::BK + key;
-            if (kk < it.kv_len) {
-                kst[i] = *reinterpret_cast<const uint4 *>(kbase + (size_t)kk * kv_stride + 8 * cc);
-                vst[i] = *reinterpret_cast<const uint4 *>(vbase + (size_t)kk * kv_stride + 8 * cc);
-            } else {
-                kst[i] = make_uint4(0, 0, 0, 0);
-                vst[i] = make_uint4(0, 0, 0, 0);
-            }
-        }
-    };
-    auto lstore = [&](int buf) {
-        __bf16 *Ks = smem + buf * (T::KTILE + T::VTILE);
-        __bf16 *Vs = Ks + T::KTILE;
-#pragma unroll
-        for (int i = 0; i < T::NLOAD; ++i) {
-            const int ci = tid + i * kThreads;
-            const int key = ci / T::CPR;
-            const int cc = ci - key * T::CPR;
-            *reinterpret_cast<uint4 *>(Ks + key * T::KST + 8 * cc) = kst[i];
-            *reinterpret_cast<uint4 *>(Vs + key * T::VST + 8 * cc) = vst[i];
-        }
-    };
-
-    if (kb_begin < kb_end) {
-        gload(kb_begin);
-        lstore(0);
+    for (int i = 0; i < T::NLOAD; ++i) {
+        const int chunk = (4 * wu + i) * 64 + lane;
+        const int rr = chunk / T::CPR;
+        const int pp = chunk - rr * T::CPR;
+        grow_[i] = rr;
+        kcol[i] = 8 * (pp ^ swz_k(rr));
+        vcol[i] = 8 * (pp ^ swz_v(rr));
     }
+    const int kv_stride_i = a.num_kv_heads * HD;
+    auto issue_loads = [&](int kb, int buf) __attribute__((always_inline)) {
+        const size_t blk = (size_t)kb * T::BK * kv_stride_i;
+        const __bf16 *kb_ptr = kbase + blk;
+        const __bf16 *vb_ptr = vbase + blk;
+        const int last = it.kv_len - 1 - kb * T::BK;
+        char *stage = smem + buf * T::STAGE_BYTES;
+#pragma unroll
+        for (int i = 0; i < T::NLOAD; ++i) {
+            const int row = min(grow_[i], last);
+            const unsigned koff = (unsigned)(row * kv_stride_i + kcol[i]);
+            const unsigned voff = (unsigned)(row * kv_stride_i + vcol[i]);
+            char *dk = stage + (4 * wu + i) * 1024;
+            __builtin_amdgcn_global_load_lds((const void *)(kb_ptr + koff),
+                                             (__attribute__((address_space(3))) void *)dk, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)(vb_ptr + voff),
+                                             (__attribute__((address_space(3))) void *)(dk + T::TILE_BYTES),
+                                             16, 0, 0);
+        }
+    };
+
+    if (kb_begin < kb_end)
+        issue_loads(kb_begin, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    const int grp = lane >> 4;
-    const int s16 = lane & 15;
-
-    for (int kb = kb_begin; kb < kb_end; ++kb) {
-        const int buf = (kb - kb_begin) & 1;
-        const bool more = kb + 1 < kb_end;
-        if (more)
-            gload(kb + 1);
-
-        const __bf16 *Ks = smem + buf * (T::KTILE + T::VTILE);
-        const __bf16 *Vs = Ks + T::KTILE;
-
-        // ---- S^T = K Q^T ----
-        f32x16 s[T::NB];
-#pragma unroll
-        for (int n = 0; n < T::NB; ++n)
-#pragma unroll
-            for (int j = 0; j < 16; ++j)
-                s[n][j] = 0.0f;
-#pragma unroll
-        for (int ds = 0; ds < T::DS; ++ds) {
-#pragma unroll
-            for (int n = 0; n < T::NB; ++n) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(
-                    Ks + (32 * n + qc) * T::KST + 16 * ds + 8 * h);
-                s[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], s[n], 0, 0, 0);
-            }
+    // Blocks below the first row's causal limit need no mask; they come
+    // first.  The rest (diagonal and KV tail) are masked.  Each range runs as
+    // its own loop over one block_step variant.
+    const int kb_mask = min(max(it.lim_first / T::BK, kb_begin), kb_end);
+    auto run = [&](auto mask_tag, auto hilo_tag, int kb_from, int kb_to) __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        constexpr bool HILO = decltype(hilo_tag)::value;
+        for (int kb = kb_from; kb < kb_to; ++kb) {
+            const int buf = (kb - kb_begin) & 1;
+            if (kb + 1 < kb_end)
+                issue_loads(kb + 1, buf ^ 1);
+            const char *Ks = smem + buf * T::STAGE_BYTES;
+            const char *Vs = Ks + T::TILE_BYTES;
+            const int thr = lim_row - kb * T::BK - 4 * h;
+            block_step<HD, POS_SCALE, MASK, HILO>(st, Ks, Vs, c, thr, qc, h, grp, s16);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
         }
-
-        // ---- mask + online softmax ----
-        const int key0 = kb * T::BK;
-        const bool need_mask = key0 + T::BK > it.lim_first;
-        const bool hilo = hilo_all || need_mask;
-        float p[T::NB][16];
-        float mx = -INFINITY;
-        if (POS_SCALE) {
-            if (need_mask) {
-#pragma unroll
-                for (int n = 0; n < T::NB; ++n)
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        const int key = key0 + 32 * n + 8 * (j >> 2) + 4 * h + (j & 3);
-                        if (key >= lim_row)
-                            s[n][j] = -INFINITY;
-                    }
-            }
-#pragma unroll
-            for (int n = 0; n < T::NB; ++n)
-#pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    mx = fmaxf(mx, s[n][j]);
-            mx = pair_max(mx) * c;
-        } else {
-#pragma unroll
-            for (int n = 0; n < T::NB; ++n)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    float x = s[n][j] * c;
-                    if (need_mask) {
-                        const int key = key0 + 32 * n + 8 * (j >> 2) + 4 * h + (j & 3);
-                        if (key >= lim_row)
-                            x = -INFINITY;
-                    }
-                    s[n][j] = x;
-                    mx = fmaxf(mx, x);
-                }
-            mx = pair_max(mx);
-        }
-        const float m_new = fmaxf(m, mx);
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        const float alpha = fast_exp2(m - m_use);
-        float psum = 0.0f;
-#pragma unroll
-        for (int n = 0; n < T::NB; ++n)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const float x = POS_SCALE ? __builtin_fmaf(s[n][j], c, -m_use) : s[n][j] - m_use;
-                p[n][j] = fast_exp2(x);
-                psum += p[n][j];
-            }
-        l = l * alpha + psum;
-        m = m_new;
-        if (__any(alpha != 1.0f)) {
-#pragma unroll
-            for (int db = 0; db < T::DB; ++db)
-#pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    acc[db][j] *= alpha;
-        }
-
-        // ---- P to bf16 (B operand of O^T += V^T P^T) ----
-        // MFMA k-step t of key row block n: lane half h, element e holds key
-        // 32 n + 16 t + 4 h + 8 (e / 4) + e % 4 — the keys this lane already
-        // holds in S^T registers j = 8 t + e.
-        bf16x8 ph[T::NB][2], pl[T::NB][2];
-#pragma unroll
-        for (int n = 0; n < T::NB; ++n)
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float pv = p[n][8 * t + e];
-                    const __bf16 hb = (__bf16)pv;
-                    ph[n][t][e] = hb;
-                    pl[n][t][e] = (__bf16)(pv - (float)hb);
-                }
-
-        // ---- O^T += V^T P^T ----
-        // A operand: lane (h, d = 32 db + lane % 32) needs V[key][d] for the
-        // 8 keys above; two LDS transpose reads each deliver 4 consecutive keys.
-#pragma unroll
-        for (int db = 0; db < T::DB; ++db) {
-#pragma unroll
-            for (int n = 0; n < T::NB; ++n) {
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const __bf16 *vp = Vs + (32 * n + 16 * t + 4 * h + (s16 >> 2)) * T::VST +
-                                       32 * db + 16 * (grp & 1) + 4 * (s16 & 3);
-                    const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4 *)((__attribute__((address_space(3))) __bf16 *)vp));
-                    const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4 *)((__attribute__((address_space(3))) __bf16 *)(vp + 8 * T::VST)));
-                    // join the two 4-key halves as one 16-byte vector (element-wise
-                    // inserts into a bf16 vector are not lowered reliably)
-                    const i16x8 v01 = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-                    const bf16x8 vf = __builtin_bit_cast(bf16x8, v01);
-                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, ph[n][t], acc[db], 0, 0, 0);
-                    if (hilo)
-                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl[n][t], acc[db], 0, 0, 0);
-                }
-            }
-        }
-
-        if (more)
-            lstore(buf ^ 1);
-        __syncthreads();
-    }
+    };
+    if (hilo_all)
+        run(std::false_type{}, std::true_type{}, kb_begin, kb_mask);
+    else
+        run(std::false_type{}, std::false_type{}, kb_begin, kb_mask);
+    run(std::true_type{}, std::true_type{}, kb_mask, kb_end);
 
     // ---- epilogue ----
-    const float lt = pair_sum(l);
+    const float lt = pair_sum(st.l);
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-    const float lse2 = lt > 0.0f ? m + log2f(lt) : -INFINITY;
+    const float lse2 = lt > 0.0f ? st.m + log2f(lt) : -INFINITY;
     if (!row_valid)
         return;
     if (it.slot < 0) {
@@ -349,7 +401,7 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, __bf16 *smem
                 bf16x4 ov;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    ov[e] = (__bf16)(acc[db][4 * jj + e] * inv);
+                    ov[e] = (__bf16)(st.acc[db][4 * jj + e] * inv);
                 *reinterpret_cast<bf16x4 *>(op + 32 * db + 8 * jj) = ov;
             }
         if (h == 0 && a.lse != nullptr)
@@ -361,10 +413,10 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, __bf16 *smem
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 float4 ov;
-                ov.x = acc[db][4 * jj + 0] * inv;
-                ov.y = acc[db][4 * jj + 1] * inv;
-                ov.z = acc[db][4 * jj + 2] * inv;
-                ov.w = acc[db][4 * jj + 3] * inv;
+                ov.x = st.acc[db][4 * jj + 0] * inv;
+                ov.y = st.acc[db][4 * jj + 1] * inv;
+                ov.z = st.acc[db][4 * jj + 2] * inv;
+                ov.w = st.acc[db][4 * jj + 3] * inv;
                 *reinterpret_cast<float4 *>(pp + 32 * db + 8 * jj) = ov;
             }
         if (h == 0)
@@ -375,8 +427,7 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, __bf16 *smem
 template <int HD>
 __global__ __launch_bounds__(kThreads, HD == 128 ? 2 : 1) void tile_kernel(TileArgs a)
 {
-    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-    __bf16 *smem = reinterpret_cast<__bf16 *>(smem_raw);
+    extern __shared__ __attribute__((aligned(16))) char smem[];
     const Item it = a.items[blockIdx.x];
     if (a.scale_log2 > 0.0f)
         tile_body<HD, true>(a, it, smem);
