@@ -62,11 +62,14 @@ struct Tile {
 };
 
 // LDS layout: chunk c (16 bytes) of key row r sits at chunk position
-// c ^ swz(r) of that row.  K rows are read 8 rows at a time at one chunk
-// (swizzle r & 7); V rows 4 at a time over two adjacent chunks by the
-// transpose read (swizzle 2 (r & 3)).  Both patterns then touch distinct banks.
-__device__ inline int swz_k(int r) { return r & 7; }
-__device__ inline int swz_v(int r) { return (r & 3) << 1; }
+// c ^ swz(r) of that row (rows are 256 or 512 bytes, a multiple of the 64
+// four-byte banks).  K is read 16 rows at a time at one chunk (128-bit reads
+// are served 16 lanes per cycle): swizzle r & 15 puts those rows on distinct
+// 16-byte slots.  V is read by the transpose read, 32 lanes per cycle over 4
+// rows x 4 adjacent chunks: swizzle 4 (r & 3) moves each row to its own
+// 4-chunk group.
+__device__ inline int swz_k(int r) { return r & 15; }
+__device__ inline int swz_v(int r) { return (r & 3) << 2; }
 
 __device__ inline float pair_max(float x)
 {
@@ -136,14 +139,27 @@ __device__ __attribute__((always_inline)) inline void block_step(
 #pragma unroll
         for (int j = 0; j < 16; ++j)
             s[n][j] = 0.0f;
-#pragma unroll
-    for (int ds = 0; ds < T::DS; ++ds) {
+    // K fragments are read one k-step ahead of the MFMAs that use them
+    bf16x8 kf[2][T::NB];
+    auto kread = [&](int ds, int slot) __attribute__((always_inline)) {
 #pragma unroll
         for (int n = 0; n < T::NB; ++n) {
             const int row = 32 * n + qc;
-            const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(
+            kf[slot][n] = *reinterpret_cast<const bf16x8 *>(
                 Ks + row * T::RB + 16 * ((2 * ds + h) ^ swz_k(row)));
-            s[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, st.qf[ds], s[n], 0, 0, 0);
+        }
+    };
+    kread(0, 0);
+#pragma unroll
+    for (int ds = 0; ds < T::DS; ++ds) {
+        if (ds + 1 < T::DS)
+            kread(ds + 1, (ds + 1) & 1);
+#pragma unroll
+        for (int n = 0; n < T::NB; ++n)
+            s[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds & 1][n], st.qf[ds], s[n], 0, 0, 0);
+        if (ds + 1 < T::DS) {
+            __builtin_amdgcn_sched_group_barrier(0x100, T::NB, 0);  // next k-step's LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x008, T::NB, 0);  // this k-step's MFMAs
         }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -187,7 +203,8 @@ __device__ __attribute__((always_inline)) inline void block_step(
             const float x = POS_SCALE ? __builtin_fmaf(s[n][j], c, -m_use) : s[n][j] - m_use;
             p[n][j] = fast_exp2(x);
         }
-    // row-sum part of this lane: fixed pairwise tree
+    // row-sum part of this lane, from the fp32 P (the LSE needs it exact):
+    // fixed pairwise tree
     float t8[T::NB * 8];
 #pragma unroll
     for (int n = 0; n < T::NB; ++n)
@@ -199,7 +216,6 @@ __device__ __attribute__((always_inline)) inline void block_step(
 #pragma unroll
         for (int j = 0; j < w; ++j)
             t8[j] = t8[2 * j] + t8[2 * j + 1];
-    const float psum = t8[0];
     if (__any(grow)) {
         const float alpha = fast_exp2(st.m - m_use);   // 1 where the reference stays, 0 at the start
         st.l *= alpha;
@@ -209,7 +225,7 @@ __device__ __attribute__((always_inline)) inline void block_step(
             for (int j = 0; j < 16; ++j)
                 st.acc[db][j] *= alpha;
     }
-    st.l += psum;
+    st.l += t8[0];
     st.m = m_ref;
 
     // P as the B operand of O^T += V^T P^T: k-step t of row block n takes,
@@ -302,6 +318,12 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
             }
         }
     }
+    // Consume the Q fragments here so that the compiler's wait for these
+    // loads is placed before the key loop; inside the loop any vmcnt wait
+    // would also wait for the K/V prefetch in flight.
+#pragma unroll
+    for (int ds = 0; ds < T::DS; ++ds)
+        asm volatile("" :: "v"(st.qf[ds]));
 #pragma unroll
     for (int db = 0; db < T::DB; ++db)
 #pragma unroll
@@ -336,23 +358,27 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
         vcol[i] = 8 * (pp ^ swz_v(rr));
     }
     const int kv_stride_i = a.num_kv_heads * HD;
+    const unsigned lds_base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
     auto issue_loads = [&](int kb, int buf) __attribute__((always_inline)) {
         const size_t blk = (size_t)kb * T::BK * kv_stride_i;
         const __bf16 *kb_ptr = kbase + blk;
         const __bf16 *vb_ptr = vbase + blk;
         const int last = it.kv_len - 1 - kb * T::BK;
-        char *stage = smem + buf * T::STAGE_BYTES;
 #pragma unroll
         for (int i = 0; i < T::NLOAD; ++i) {
             const int row = min(grow_[i], last);
-            const unsigned koff = (unsigned)(row * kv_stride_i + kcol[i]);
-            const unsigned voff = (unsigned)(row * kv_stride_i + vcol[i]);
-            char *dk = stage + (4 * wu + i) * 1024;
-            __builtin_amdgcn_global_load_lds((const void *)(kb_ptr + koff),
-                                             (__attribute__((address_space(3))) void *)dk, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void *)(vb_ptr + voff),
-                                             (__attribute__((address_space(3))) void *)(dk + T::TILE_BYTES),
-                                             16, 0, 0);
+            const unsigned koff = (unsigned)(row * kv_stride_i + kcol[i]) * 2u;
+            const unsigned voff = (unsigned)(row * kv_stride_i + vcol[i]) * 2u;
+            const unsigned dk = lds_base + (unsigned)(buf * T::STAGE_BYTES + (4 * wu + i) * 1024);
+            // global_load_lds_dwordx4: lane l's 16 bytes land at M0 + 16 l.
+            // Issued as inline asm so that the compiler does not order the
+            // LDS reads of the current buffer behind these loads; the wait
+            // for them is the explicit vmcnt(0) before the block barrier.
+            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                         :: "s"(dk), "v"(koff), "s"(kb_ptr) : "memory", "m0");
+            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                         :: "s"(dk + (unsigned)T::TILE_BYTES), "v"(voff), "s"(vb_ptr)
+                         : "memory", "m0");
         }
     };
 
