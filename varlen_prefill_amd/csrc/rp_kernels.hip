@@ -139,27 +139,50 @@ __device__ __attribute__((always_inline)) inline void block_step(
 #pragma unroll
         for (int j = 0; j < 16; ++j)
             s[n][j] = 0.0f;
-    // K fragments are read one k-step ahead of the MFMAs that use them
-    bf16x8 kf[2][T::NB];
-    auto kread = [&](int ds, int slot) __attribute__((always_inline)) {
+    // All K fragments of the block are requested up front; the MFMAs then
+    // consume them in arrival order.
+    bf16x8 kf[T::DS][T::NB];
+#pragma unroll
+    for (int ds = 0; ds < T::DS; ++ds)
 #pragma unroll
         for (int n = 0; n < T::NB; ++n) {
             const int row = 32 * n + qc;
-            kf[slot][n] = *reinterpret_cast<const bf16x8 *>(
+            kf[ds][n] = *reinterpret_cast<const bf16x8 *>(
                 Ks + row * T::RB + 16 * ((2 * ds + h) ^ swz_k(row)));
         }
-    };
-    kread(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ds = 0; ds < T::DS; ++ds) {
-        if (ds + 1 < T::DS)
-            kread(ds + 1, (ds + 1) & 1);
+    for (int ds = 0; ds < T::DS; ++ds)
 #pragma unroll
         for (int n = 0; n < T::NB; ++n)
-            s[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds & 1][n], st.qf[ds], s[n], 0, 0, 0);
-        if (ds + 1 < T::DS) {
-            __builtin_amdgcn_sched_group_barrier(0x100, T::NB, 0);  // next k-step's LDS reads
-            __builtin_amdgcn_sched_group_barrier(0x008, T::NB, 0);  // this k-step's MFMAs
+            s[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds][n], st.qf[ds], s[n], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // The V fragments of the PV product are requested now and arrive while
+    // the softmax runs.  A operand: lane (h, d = 32 db + lane % 32) needs
+    // V[key][d] for the 8 keys of the P operand below; each LDS transpose
+    // read delivers 4 consecutive keys.
+    bf16x8 vf[T::DB][T::NB][2];
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db) {
+#pragma unroll
+        for (int n = 0; n < T::NB; ++n) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                // source lane s16 of each 16-lane group reads key row
+                // 32 n + 16 t + 4 h + s16 / 4 (and 8 rows further), d = 32 db +
+                // 16 (grp & 1) + 4 (s16 & 3): chunk c, byte 8 (s16 & 1) within it
+                const int row = 32 * n + 16 * t + 4 * h + (s16 >> 2);
+                const int cc = 4 * db + 2 * (grp & 1) + ((s16 & 3) >> 1);
+                const char *vp = Vs + row * T::RB + 16 * (cc ^ swz_v(row)) + 8 * (s16 & 1);
+                const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4 *)((__attribute__((address_space(3))) char *)vp));
+                const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4 *)((__attribute__((address_space(3))) char *)(vp + 8 * T::RB)));
+                // join the two 4-key halves as one 16-byte vector (element-wise
+                // inserts into a bf16 vector are not lowered reliably)
+                const i16x8 v01 = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+                vf[db][n][t] = __builtin_bit_cast(bf16x8, v01);
+            }
         }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -247,34 +270,16 @@ __device__ __attribute__((always_inline)) inline void block_step(
             }
 
     __builtin_amdgcn_sched_barrier(0);
-    // A operand: lane (h, d = 32 db + lane % 32) needs V[key][d] for the 8
-    // keys above; each LDS transpose read delivers 4 consecutive keys.
 #pragma unroll
-    for (int db = 0; db < T::DB; ++db) {
+    for (int db = 0; db < T::DB; ++db)
 #pragma unroll
-        for (int n = 0; n < T::NB; ++n) {
+        for (int n = 0; n < T::NB; ++n)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                // source lane s16 of each 16-lane group reads key row
-                // 32 n + 16 t + 4 h + s16 / 4 (and 8 rows further), d = 32 db +
-                // 16 (grp & 1) + 4 (s16 & 3): chunk c, byte 8 (s16 & 1) within it
-                const int row = 32 * n + 16 * t + 4 * h + (s16 >> 2);
-                const int cc = 4 * db + 2 * (grp & 1) + ((s16 & 3) >> 1);
-                const char *vp = Vs + row * T::RB + 16 * (cc ^ swz_v(row)) + 8 * (s16 & 1);
-                const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4 *)((__attribute__((address_space(3))) char *)vp));
-                const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4 *)((__attribute__((address_space(3))) char *)(vp + 8 * T::RB)));
-                // join the two 4-key halves as one 16-byte vector (element-wise
-                // inserts into a bf16 vector are not lowered reliably)
-                const i16x8 v01 = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-                const bf16x8 vf = __builtin_bit_cast(bf16x8, v01);
-                st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, ph[n][t], st.acc[db], 0, 0, 0);
+                st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db][n][t], ph[n][t], st.acc[db], 0, 0, 0);
                 if (HILO)
-                    st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl[n][t], st.acc[db], 0, 0, 0);
+                    st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db][n][t], pl[n][t], st.acc[db], 0, 0, 0);
             }
-        }
-    }
 }
 
 template <int HD, bool POS_SCALE>
