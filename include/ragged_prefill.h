@@ -107,7 +107,8 @@ typedef struct rp_plan rp_plan;
 
 enum rp_split_mode {
     RP_SPLIT_AUTO = 0,    /* split long KV across workgroups only when the batch is small */
-    RP_SPLIT_NEVER = 1,   /* one workgroup per tile, folding KV chunks in order */
+    RP_SPLIT_NEVER = 1,   /* one workgroup per tile, folding KV chunks in order
+                             (not implemented: rp_plan_create returns RP_EUNSUPPORTED) */
     RP_SPLIT_ALWAYS = 2   /* one workgroup per (tile, KV chunk) + merge kernel */
 };
 
@@ -115,7 +116,7 @@ enum rp_split_mode {
  * numerics (where partial states are cut and merged); the split mode only
  * moves work between workgroups and never changes a bit of the results. */
 typedef struct rp_plan_opts {
-    int kv_chunk;    /* canonical KV chunk in keys (multiple of 64, >= 64); 0 = default 2048 */
+    int kv_chunk;    /* canonical KV chunk in keys (multiple of 64, >= 64); 0 = default 8192 */
     int split_mode;  /* enum rp_split_mode */
     int host_only;   /* nonzero: plan on the host only; such a plan can be inspected, not run */
     int reserved;
