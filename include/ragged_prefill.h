@@ -106,7 +106,7 @@ int ragged_prefill_bf16(const void *q, const void *k, const void *v, void *o, fl
 typedef struct rp_plan rp_plan;
 
 enum rp_split_mode {
-    RP_SPLIT_AUTO = 0,    /* split long KV across workgroups only when the batch is small */
+    RP_SPLIT_AUTO = 0,    /* split every tile whose visible keys span more than one KV chunk */
     RP_SPLIT_NEVER = 1,   /* one workgroup per tile, folding KV chunks in order
                              (not implemented: rp_plan_create returns RP_EUNSUPPORTED) */
     RP_SPLIT_ALWAYS = 2   /* one workgroup per (tile, KV chunk) + merge kernel */
@@ -119,7 +119,9 @@ typedef struct rp_plan_opts {
     int kv_chunk;    /* canonical KV chunk in keys (multiple of 64, >= 64); 0 = default 8192 */
     int split_mode;  /* enum rp_split_mode */
     int host_only;   /* nonzero: plan on the host only; such a plan can be inspected, not run */
-    int reserved;
+    int num_xcds;    /* XCDs the launch order is arranged for (workgroup b runs on XCD
+                        b % num_xcds); 0 = default (8, the MI355X XCD count, for
+                        head_dim 128; 1 for head_dim 256), 1 = plain longest-first order */
 } rp_plan_opts;
 
 /* Summary of a plan (host side). */
@@ -151,8 +153,9 @@ int rp_plan_get_info(const rp_plan *plan, rp_plan_info *info);
 size_t rp_plan_workspace_bytes(const rp_plan *plan);
 
 /* Host copy of the tile worklist: RP_ITEM_INTS int32 per item, in launch
- * order (for inspection and tests).  capacity counts items. Returns the number
- * of items copied (>= 0) or a negative status. */
+ * order (for inspection and tests); items with n_tok = 0 (second int) are
+ * padding that does nothing.  capacity counts items.  Returns the number of
+ * items copied (>= 0) or a negative status. */
 #define RP_ITEM_INTS 16
 int64_t rp_plan_copy_items(const rp_plan *plan, int32_t *dst, int64_t capacity);
 

@@ -25,12 +25,23 @@ def _limit(i, qo, kv, causal):
     return min(max(i + kv - qo + 1, 0), kv)
 
 
-def _check_plan(qo_lens, kv_lens, hq, hkv, d, causal, kv_chunk=0, q_base=0, kv_base=0):
+def _check_plan(qo_lens, kv_lens, hq, hkv, d, causal, kv_chunk=0, q_base=0, kv_base=0,
+                num_xcds=0):
     qi = indptr_from_lens(qo_lens, q_base)
     ki = indptr_from_lens(kv_lens, kv_base)
-    p = vp.Plan(qi, ki, hq, hkv, d, causal, kv_chunk=kv_chunk, host_only=True)
+    p = vp.Plan(qi, ki, hq, hkv, d, causal, kv_chunk=kv_chunk, host_only=True, num_xcds=num_xcds)
     info = p.info
-    items = p.items()
+    launch = p.items()
+    xcds = num_xcds or (8 if d == 128 else 1)
+    # longest-first within each XCD's share of the launch order (workgroup b
+    # runs on XCD b % xcds); padding items (n_tok = 0) carry no work
+    for x in range(xcds):
+        mine = launch[x::xcds]
+        mine = mine[mine[:, F["n_tok"]] > 0]
+        assert np.all(mine[:-1, F["cost"]] >= mine[1:, F["cost"]])
+    pad = launch[launch[:, F["n_tok"]] == 0]
+    assert np.all(pad[:, F["key_end"]] <= pad[:, F["key_begin"]])
+    items = launch[launch[:, F["n_tok"]] > 0]
     chunk = info["kv_chunk"]
     g = hq // hkv
     tt = 128 // g
@@ -70,9 +81,6 @@ def _check_plan(qo_lens, kv_lens, hq, hkv, d, causal, kv_chunk=0, q_base=0, kv_b
         assert it[F["q_tok0"]] == qi[b] + it[F["t0"]]
         assert it[F["kv_row0"]] == ki[b]
         assert it[F["t0"]] + it[F["n_tok"]] <= qo_lens[b]
-    # longest first
-    costs = items[:, F["cost"]]
-    assert np.all(costs[:-1] >= costs[1:])
     # algorithmic work
     pairs = sum(_limit(i, qo, kv, causal) for qo, kv in zip(qo_lens, kv_lens) for i in range(qo))
     assert info["flops"] == pytest.approx(4.0 * d * hq * pairs, rel=1e-12)
@@ -131,3 +139,28 @@ def test_workspace_size_counts_partial_states():
     n_slots = int(np.sum(items[:, F["slot"]] >= 0))
     assert n_slots == 2 * 2 * 5  # two 32-token tiles x two kv heads x five chunks
     assert p.workspace_bytes >= n_slots * 128 * (128 + 1) * 4
+
+
+def test_xcd_grouping_keeps_tiles_of_one_kv_head_together():
+    c = CONFIGS["hd128_gqa_causal"]
+    p, _ = _check_plan(c.qo_lens, c.kv_lens, 32, 8, 128, True)
+    launch = p.items()
+    homes = {}
+    costs = np.zeros(8)
+    for b, it in enumerate(launch):
+        if it[F["n_tok"]] == 0:
+            continue
+        homes.setdefault((it[F["request"]], it[F["kv_head"]]), set()).add(b % 8)
+        costs[b % 8] += it[F["cost"]]
+    # most (request, kv head) groups live on a single XCD; loads are balanced
+    single = sum(1 for v in homes.values() if len(v) == 1)
+    assert single >= 0.6 * len(homes)
+    assert costs.max() <= 1.02 * costs.mean() + launch[:, F["cost"]].max()
+
+
+def test_single_xcd_order_is_plain_longest_first():
+    c = CONFIGS["ragged64"]
+    p, _ = _check_plan(c.qo_lens, c.kv_lens, 32, 8, 128, True, num_xcds=1)
+    launch = p.items()
+    assert np.all(launch[:, F["n_tok"]] > 0)
+    assert np.all(launch[:-1, F["cost"]] >= launch[1:, F["cost"]])

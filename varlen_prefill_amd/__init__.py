@@ -104,7 +104,7 @@ class Plan:
 
     def __init__(self, q_indptr, kv_indptr, num_qo_heads: int, num_kv_heads: int, head_dim: int,
                  causal: bool = True, kv_chunk: int = 0, split_mode: int = RP_SPLIT_AUTO,
-                 host_only: bool = False):
+                 host_only: bool = False, num_xcds: int = 0):
         lib = _lib.load()
         self._lib = lib
         self.q_indptr = _host_indptr(q_indptr)
@@ -116,7 +116,7 @@ class Plan:
         self.num_kv_heads = int(num_kv_heads)
         self.head_dim = int(head_dim)
         self.causal = bool(causal)
-        opts = RpPlanOpts(int(kv_chunk), int(split_mode), 1 if host_only else 0, 0)
+        opts = RpPlanOpts(int(kv_chunk), int(split_mode), 1 if host_only else 0, int(num_xcds))
         handle = ctypes.c_void_p()
         st = lib.rp_plan_create(_ptr(self.q_indptr), _ptr(self.kv_indptr), self.batch,
                                 self.num_qo_heads, self.num_kv_heads, self.head_dim,

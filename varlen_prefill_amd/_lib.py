@@ -45,7 +45,7 @@ EXPORTS = [
 
 class RpPlanOpts(ctypes.Structure):
     _fields_ = [("kv_chunk", ctypes.c_int), ("split_mode", ctypes.c_int),
-                ("host_only", ctypes.c_int), ("reserved", ctypes.c_int)]
+                ("host_only", ctypes.c_int), ("num_xcds", ctypes.c_int)]
 
 
 class RpPlanInfo(ctypes.Structure):

@@ -133,6 +133,7 @@ int create_plan(const int32_t *q_indptr, const int32_t *kv_indptr, int batch, in
     shape.causal = causal ? 1 : 0;
     shape.kv_chunk = opts ? opts->kv_chunk : 0;
     shape.split_mode = opts ? opts->split_mode : 0;
+    shape.num_xcds = opts ? opts->num_xcds : 0;
     rp_plan *p = new (std::nothrow) rp_plan;
     if (p == nullptr)
         return fail(RP_ENOMEM, "out of host memory");

@@ -26,6 +26,7 @@ constexpr int kThreads = 256;       // threads per tile workgroup
 constexpr int kMergeThreads = 256;  // threads per merge workgroup
 constexpr int kDefaultKvChunk = 8192;
 constexpr int kChunkAlign = 64;     // kv_chunk must be a multiple of this
+constexpr int kDefaultXcds = 8;     // MI355X: 8 XCDs, workgroups dispatched round-robin
 // Key blocks are computed with P split into a bf16 hi part and a bf16 lo
 // remainder when the block is partially masked for the tile or when the
 // tile's first row sees at most this many keys.
@@ -36,7 +37,7 @@ inline constexpr int key_block(int head_dim) { return head_dim == 128 ? 64 : 32;
 // Work item of the tile kernel: 16 int32 (64 bytes).
 struct Item {
     int32_t q_tok0;     // global row (in Q/O) of the tile's first token
-    int32_t n_tok;      // tokens in the tile (>= 1)
+    int32_t n_tok;      // tokens in the tile (>= 1; 0 marks an empty padding item)
     int32_t t0;         // request-relative index of the first token
     int32_t qo_len;     // request's query length
     int32_t kv_row0;    // global row (in K/V) of the request's key 0

@@ -308,35 +308,6 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
         lim_row = lr < 0 ? 0 : (lr > it.kv_len ? it.kv_len : lr);
     }
 
-    WaveState<HD> st;
-    {
-        const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(
-            static_cast<const __bf16 *>(a.q) + q_row * HD + 8 * h);
-#pragma unroll
-        for (int ds = 0; ds < T::DS; ++ds) {
-            if (row_valid) {
-                st.qf[ds] = qp[2 * ds];
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    st.qf[ds][e] = (__bf16)0.0f;
-            }
-        }
-    }
-    // Consume the Q fragments here so that the compiler's wait for these
-    // loads is placed before the key loop; inside the loop any vmcnt wait
-    // would also wait for the K/V prefetch in flight.
-#pragma unroll
-    for (int ds = 0; ds < T::DS; ++ds)
-        asm volatile("" :: "v"(st.qf[ds]));
-#pragma unroll
-    for (int db = 0; db < T::DB; ++db)
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-            st.acc[db][j] = 0.0f;
-    st.m = -INFINITY;
-    st.l = 0.0f;
-
     const float c = a.scale_log2;
     const int kb_begin = it.key_begin / T::BK;
     const int kb_end = it.key_end > it.key_begin ? (it.key_end + T::BK - 1) / T::BK : kb_begin;
@@ -387,8 +358,40 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
         }
     };
 
+    // The first block's K/V loads go out before the Q loads so that the two
+    // latencies overlap.
     if (kb_begin < kb_end)
         issue_loads(kb_begin, 0);
+
+    WaveState<HD> st;
+    {
+        const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(
+            static_cast<const __bf16 *>(a.q) + q_row * HD + 8 * h);
+#pragma unroll
+        for (int ds = 0; ds < T::DS; ++ds) {
+            if (row_valid) {
+                st.qf[ds] = qp[2 * ds];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    st.qf[ds][e] = (__bf16)0.0f;
+            }
+        }
+    }
+    // Consume the Q fragments here so that the compiler's wait for these
+    // loads is placed before the key loop; inside the loop any vmcnt wait
+    // would also wait for the K/V prefetch in flight.
+#pragma unroll
+    for (int ds = 0; ds < T::DS; ++ds)
+        asm volatile("" :: "v"(st.qf[ds]));
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            st.acc[db][j] = 0.0f;
+    st.m = -INFINITY;
+    st.l = 0.0f;
+
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
@@ -460,6 +463,8 @@ __global__ __launch_bounds__(kThreads, HD == 128 ? 2 : 1) void tile_kernel(TileA
 {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const Item it = a.items[blockIdx.x];
+    if (it.n_tok == 0)
+        return;  // padding item of the launch order
     if (a.scale_log2 > 0.0f)
         tile_body<HD, true>(a, it, smem);
     else

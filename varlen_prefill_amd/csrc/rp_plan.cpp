@@ -16,7 +16,9 @@
 #include "rp_plan.h"
 
 #include <algorithm>
+#include <map>
 #include <numeric>
+#include <tuple>
 
 namespace rp {
 
@@ -35,6 +37,56 @@ int64_t limit_of(int64_t i, int64_t qo_len, int64_t kv_len, bool causal)
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Launch order.  Workgroups are handed to the XCDs round-robin (workgroup b
+// runs on XCD b % X), each XCD with its own L2.  Tiles that read the same K/V
+// (same request, kv head and KV chunk) are placed on one XCD when its load
+// allows, so their K/V blocks are L2 hits; each XCD's list is longest-first
+// (LPT) and the XCD loads are balanced greedily.  Lists are interleaved into
+// one grid, padded with empty items (n_tok = 0) to equal length.
+void order_items(std::vector<Item> &items, int xcds)
+{
+    std::stable_sort(items.begin(), items.end(),
+                     [](const Item &x, const Item &y) { return x.cost > y.cost; });
+    if (xcds <= 1 || items.size() < 2)
+        return;
+    int64_t total = 0;
+    for (const Item &it : items)
+        total += it.cost;
+    const int64_t target = (total + xcds - 1) / xcds;
+    std::vector<int64_t> load((size_t)xcds, 0);
+    std::vector<std::vector<Item>> lists((size_t)xcds);
+    std::map<std::tuple<int, int, int, int>, int> home;  // (request, kv head, chunk, split) -> XCD
+    for (const Item &it : items) {
+        const auto key = std::make_tuple(it.request, it.kv_head, it.slot >= 0 ? it.chunk : 0,
+                                         it.slot >= 0 ? 1 : 0);
+        auto h = home.find(key);
+        int x;
+        if (h != home.end() && load[(size_t)h->second] + it.cost <= target) {
+            x = h->second;
+        } else {
+            x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+            if (h == home.end())
+                home.emplace(key, x);
+        }
+        lists[(size_t)x].push_back(it);
+        load[(size_t)x] += it.cost;
+    }
+    size_t len = 0;
+    for (const auto &l : lists)
+        len = std::max(len, l.size());
+    Item empty{};
+    empty.n_tok = 0;
+    empty.key_begin = 0;
+    empty.key_end = 0;
+    empty.slot = -1;
+    empty.request = -1;
+    items.clear();
+    items.reserve(len * (size_t)xcds);
+    for (size_t k = 0; k < len; ++k)
+        for (int x = 0; x < xcds; ++x)
+            items.push_back(k < lists[(size_t)x].size() ? lists[(size_t)x][k] : empty);
+}
 
 }  // namespace
 
@@ -88,6 +140,15 @@ int build_plan(const int32_t *q_indptr, const int32_t *kv_indptr, const PlanShap
     }
     if (shape.kv_chunk < kChunkAlign || shape.kv_chunk % kChunkAlign != 0) {
         err = "kv_chunk must be a positive multiple of 64";
+        return kEInval;
+    }
+    // Default launch order: XCD-grouped for head_dim 128, plain longest-first
+    // for head_dim 256, whose per-XCD K/V working set far exceeds an L2 and
+    // which measured ~4 % slower when grouped.
+    if (shape.num_xcds == 0)
+        shape.num_xcds = shape.head_dim == 128 ? kDefaultXcds : 1;
+    if (shape.num_xcds < 1 || shape.num_xcds > 64) {
+        err = "num_xcds must be in [1, 64] (0 = default)";
         return kEInval;
     }
     if (shape.split_mode < 0 || shape.split_mode > 2) {
@@ -203,8 +264,7 @@ int build_plan(const int32_t *q_indptr, const int32_t *kv_indptr, const PlanShap
         }
         it.cost = (int32_t)std::min<int64_t>(cost, INT32_MAX);
     }
-    std::stable_sort(plan.items.begin(), plan.items.end(),
-                     [](const Item &x, const Item &y) { return x.cost > y.cost; });
+    order_items(plan.items, shape.num_xcds);
 
     const double hd = shape.head_dim;
     plan.flops = 4.0 * hd * shape.num_qo_heads * pairs_total;

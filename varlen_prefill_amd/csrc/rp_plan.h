@@ -18,6 +18,7 @@ struct PlanShape {
     int causal = 0;
     int kv_chunk = kDefaultKvChunk;
     int split_mode = 0;  // enum rp_split_mode
+    int num_xcds = kDefaultXcds;
 };
 
 struct HostPlan {
