@@ -1,0 +1,75 @@
+"""Host-side check of the tile kernel's staging and LDS index arithmetic.
+
+Restates, for every tile shape the library compiles (head_dim 128 and 256 with
+their key-block sizes and pipeline depths), the mapping of direct-to-LDS load
+lanes to K/V chunks and the K-row and V-transpose read addresses, and checks
+that every LDS access stays inside its buffer and every chunk of a block is
+written exactly once.  Runs without a GPU; a failure here means a kernel
+change would read or write LDS out of bounds.
+"""
+
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _shape(hd):
+    text = open(os.path.join(ROOT, "varlen_prefill_amd", "csrc", "rp_internal.h")).read()
+    bk = int(re.search(rf"#define RP_HD{hd}_BK (\d+)", text).group(1))
+    st = int(re.search(rf"#define RP_HD{hd}_STAGES (\d+)", text).group(1))
+    return bk, st
+
+
+@pytest.mark.parametrize("hd", [128, 256])
+def test_staging_and_reads_stay_in_bounds(hd):
+    bk, stages = _shape(hd)
+    threads = 256
+    rb, cpr = hd * 2, hd // 8
+    tile = bk * rb
+    nload = tile // 1024 // (threads // 64)
+    assert nload * 1024 * (threads // 64) == tile
+    stage = 2 * tile
+    lds = stages * stage
+    assert lds <= 160 * 1024
+
+    def swz_k(r):
+        return r & 15
+
+    def swz_v(r):
+        return (r & 3) << 2
+
+    wk, wv = set(), set()
+    for w in range(threads // 64):
+        for i in range(nload):
+            for lane in range(64):
+                chunk = (nload * w + i) * 64 + lane
+                rr, pp = divmod(chunk, cpr)
+                assert rr < bk
+                assert 0 <= (pp ^ swz_k(rr)) < cpr and 0 <= (pp ^ swz_v(rr)) < cpr
+                dk = (nload * w + i) * 1024 + 16 * lane
+                assert dk + 16 <= tile
+                assert (stages - 1) * stage + tile + dk + 16 <= lds
+                wk.add((rr, pp ^ swz_k(rr)))
+                wv.add((rr, pp ^ swz_v(rr)))
+    assert len(wk) == bk * cpr and len(wv) == bk * cpr
+
+    nb, ds_steps, dblocks = bk // 32, hd // 16, hd // 32
+    for lane in range(64):
+        h, qc, grp, s16 = lane >> 5, lane & 31, lane >> 4, lane & 15
+        for ds in range(ds_steps):
+            for n in range(nb):
+                row = 32 * n + qc
+                pos = (2 * ds + h) ^ swz_k(row)
+                assert row < bk and 0 <= pos < cpr
+                assert row * rb + 16 * pos + 16 <= tile
+        for db in range(dblocks):
+            for n in range(nb):
+                for t in range(2):
+                    row = 32 * n + 16 * t + 4 * h + (s16 >> 2)
+                    cc = 4 * db + 2 * (grp & 1) + ((s16 & 3) >> 1)
+                    pos = cc ^ swz_v(row)
+                    assert 0 <= pos < cpr and row + 8 < bk
+                    assert (row + 8) * rb + 16 * pos + 8 * (s16 & 1) + 8 <= tile

@@ -32,7 +32,22 @@ constexpr int kDefaultXcds = 8;     // MI355X: 8 XCDs, workgroups dispatched rou
 // tile's first row sees at most this many keys.
 constexpr int kHiLoKeys = 128;
 
-inline constexpr int key_block(int head_dim) { return head_dim == 128 ? 64 : 32; }
+// Key-block shape of the tile kernel: keys per block and LDS pipeline depth
+// (stages in flight, K and V of one block per stage).
+#ifndef RP_HD128_BK
+#define RP_HD128_BK 32
+#endif
+#ifndef RP_HD128_STAGES
+#define RP_HD128_STAGES 2
+#endif
+#ifndef RP_HD256_BK
+#define RP_HD256_BK 32
+#endif
+#ifndef RP_HD256_STAGES
+#define RP_HD256_STAGES 2
+#endif
+inline constexpr int key_block(int head_dim) { return head_dim == 128 ? RP_HD128_BK : RP_HD256_BK; }
+inline constexpr int kv_stages(int head_dim) { return head_dim == 128 ? RP_HD128_STAGES : RP_HD256_STAGES; }
 
 // Work item of the tile kernel: 16 int32 (64 bytes).
 struct Item {

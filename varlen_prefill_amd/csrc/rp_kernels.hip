@@ -54,8 +54,9 @@ struct Tile {
     static constexpr int RB = HD * 2;            // bytes per K/V row in LDS (unpadded)
     static constexpr int CPR = HD / 8;           // 16-byte chunks per row
     static constexpr int TILE_BYTES = BK * RB;   // one K (or V) block
-    static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
-    static constexpr int LDS_BYTES = 2 * STAGE_BYTES;  // double-buffered K and V
+    static constexpr int STAGE_BYTES = 2 * TILE_BYTES;     // K and V of one block
+    static constexpr int STAGES = kv_stages(HD);           // blocks in flight
+    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
     // direct-to-LDS loads: one instruction moves 64 lanes x 16 bytes
     static constexpr int NLOAD = TILE_BYTES / (64 * 16) / (kThreads / 64);
     static_assert(NLOAD * 64 * 16 * (kThreads / 64) == TILE_BYTES, "block must split evenly over waves");
@@ -318,7 +319,7 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
     const __bf16 *vbase = static_cast<const __bf16 *>(a.v) + head_off;
 
     // Staging: direct-to-LDS loads.  Wave w, load i fills LDS chunks
-    // (4 w + i) * 64 + lane of the tile: key row r = chunk / CPR, position
+    // (NLOAD w + i) * 64 + lane of the tile: key row r = chunk / CPR, position
     // p = chunk % CPR, which holds global chunk p ^ swz(r).  Rows past the end
     // of the request are clamped to its last key: those keys are masked
     // (P = 0 exactly), so the data there is inert.
@@ -326,7 +327,7 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
     int grow_[T::NLOAD], kcol[T::NLOAD], vcol[T::NLOAD];
 #pragma unroll
     for (int i = 0; i < T::NLOAD; ++i) {
-        const int chunk = (4 * wu + i) * 64 + lane;
+        const int chunk = (T::NLOAD * wu + i) * 64 + lane;
         const int rr = chunk / T::CPR;
         const int pp = chunk - rr * T::CPR;
         grow_[i] = rr;
@@ -345,11 +346,11 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
             const int row = min(grow_[i], last);
             const unsigned koff = (unsigned)(row * kv_stride_i + kcol[i]) * 2u;
             const unsigned voff = (unsigned)(row * kv_stride_i + vcol[i]) * 2u;
-            const unsigned dk = lds_base + (unsigned)(buf * T::STAGE_BYTES + (4 * wu + i) * 1024);
+            const unsigned dk = lds_base + (unsigned)(buf * T::STAGE_BYTES + (T::NLOAD * wu + i) * 1024);
             // global_load_lds_dwordx4: lane l's 16 bytes land at M0 + 16 l.
             // Issued as inline asm so that the compiler does not order the
             // LDS reads of the current buffer behind these loads; the wait
-            // for them is the explicit vmcnt(0) before the block barrier.
+            // for them is the explicit vmcnt wait before the block barrier.
             asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                          :: "s"(dk), "v"(koff), "s"(kb_ptr) : "memory", "m0");
             asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
@@ -358,10 +359,24 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
         }
     };
 
-    // The first block's K/V loads go out before the Q loads so that the two
-    // latencies overlap.
-    if (kb_begin < kb_end)
-        issue_loads(kb_begin, 0);
+    // Wait until at most `later` blocks' loads (issued after the one needed
+    // next) are still in flight: vmcnt counts this wave's outstanding loads,
+    // 2 NLOAD per block.
+    auto wait_loads = [&](int later) __attribute__((always_inline)) {
+        static_assert(T::STAGES <= 4, "extend the wait cases");
+        if (T::STAGES > 3 && later >= 2)
+            asm volatile("s_waitcnt vmcnt(%0)" :: "n"(4 * T::NLOAD) : "memory");
+        else if (T::STAGES > 2 && later >= 1)
+            asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * T::NLOAD) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
+
+    // The first blocks' K/V loads go out before the Q loads so that the
+    // latencies overlap.  Block kb lives in stage (kb - kb_begin) % STAGES.
+    const int kb_pre = min(kb_begin + T::STAGES - 1, kb_end);
+    for (int kb = kb_begin; kb < kb_pre; ++kb)
+        issue_loads(kb, kb - kb_begin);
 
     WaveState<HD> st;
     {
@@ -392,7 +407,7 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
     st.m = -INFINITY;
     st.l = 0.0f;
 
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_loads(kb_pre - kb_begin - 1);
     __syncthreads();
 
     // Blocks below the first row's causal limit need no mask; they come
@@ -403,14 +418,15 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
         constexpr bool MASK = decltype(mask_tag)::value;
         constexpr bool HILO = decltype(hilo_tag)::value;
         for (int kb = kb_from; kb < kb_to; ++kb) {
-            const int buf = (kb - kb_begin) & 1;
-            if (kb + 1 < kb_end)
-                issue_loads(kb + 1, buf ^ 1);
+            const int buf = (kb - kb_begin) % T::STAGES;
+            if (kb + T::STAGES - 1 < kb_end)
+                issue_loads(kb + T::STAGES - 1, (kb + T::STAGES - 1 - kb_begin) % T::STAGES);
             const char *Ks = smem + buf * T::STAGE_BYTES;
             const char *Vs = Ks + T::TILE_BYTES;
             const int thr = lim_row - kb * T::BK - 4 * h;
             block_step<HD, POS_SCALE, MASK, HILO>(st, Ks, Vs, c, thr, qc, h, grp, s16);
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            // block kb + 1 must have landed; later ones may stay in flight
+            wait_loads(min(kb_end, kb + T::STAGES) - (kb + 2));
             __syncthreads();
         }
     };
