@@ -16,6 +16,13 @@ Default workload: 8 requests, qo_len = kv_len ~ U[128, 2048] (recorded lengths),
 Other modes:
   --copy-probe-mib M   run a plain device copy of M MiB (read M, write M) a few
                        times; used to scale rocprofv3 FETCH_SIZE/WRITE_SIZE.
+  --record-traffic KDIR CDIR
+                       (no GPU) turn the rocprofv3 counter CSVs of the
+                       workload's run (KDIR: fetch_/write_counter_collection.csv)
+                       and of the copy probe (CDIR, same names) into
+                       profiles/traffic_<kernel>_<workload>.json, which later
+                       runs report as roofline.traffic while the kernel source
+                       is unchanged.
 """
 
 from __future__ import annotations
@@ -57,6 +64,7 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--copy-probe-mib", type=int, default=0)
+    p.add_argument("--record-traffic", nargs=2, metavar=("KDIR", "CDIR"))
     return p.parse_args()
 
 
@@ -112,6 +120,52 @@ def cpu_baseline(batch, cfg, causal: bool, sm_scale: float, target_s: float) -> 
     }
 
 
+def record_traffic(kdir: str, cdir: str, workload: str, head_dim: int, alg_bytes: float,
+                   copy_mib: int = 1024) -> str:
+    """HBM bytes per tile-kernel launch from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for the copy probe
+    of known size."""
+    import csv
+
+    def values(path, pick):
+        with open(path) as f:
+            return [float(r["Counter_Value"]) for r in csv.DictReader(f) if pick(r["Kernel_Name"])]
+
+    tile = lambda name: f"tile_kernel<{head_dim}>" in name
+    copy = lambda name: "copyBuffer" in name
+    fetch = values(os.path.join(kdir, "fetch_counter_collection.csv"), tile)
+    write = values(os.path.join(kdir, "write_counter_collection.csv"), tile)
+    cfetch = values(os.path.join(cdir, "fetch_counter_collection.csv"), copy)
+    cwrite = values(os.path.join(cdir, "write_counter_collection.csv"), copy)
+    if not (fetch and write and cfetch and cwrite):
+        raise SystemExit("record-traffic: a counter file holds no matching dispatch")
+    nbytes = copy_mib * (1 << 20)
+    fetch_scale = nbytes / (float(np.mean(cfetch)) * 1024.0)
+    write_scale = nbytes / (float(np.mean(cwrite)) * 1024.0)
+    hbm = float(np.mean(fetch)) * 1024.0 * fetch_scale + float(np.mean(write)) * 1024.0 * write_scale
+    kernel = f"tile_kernel_hd{head_dim}"
+    rec = {
+        "kernel": kernel,
+        "workload": workload,
+        "kernel_source_sha256_16": kernel_source_hash(),
+        "dispatches": len(fetch),
+        "fetch_size_kib_per_dispatch": float(np.mean(fetch)),
+        "write_size_kib_per_dispatch": float(np.mean(write)),
+        "copy_probe": {"bytes_read": nbytes, "bytes_written": nbytes,
+                       "fetch_size_kib": float(np.mean(cfetch)),
+                       "write_size_kib": float(np.mean(cwrite))},
+        "fetch_scale": fetch_scale,
+        "write_scale": write_scale,
+        "hbm_bytes_per_launch": hbm,
+        "algorithmic_bytes_per_launch": alg_bytes,
+    }
+    path = TRAFFIC_FILE.format(kernel=kernel, workload=workload)
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return path
+
+
 def load_traffic(kernel: str, workload: str):
     path = TRAFFIC_FILE.format(kernel=kernel, workload=workload)
     if not os.path.exists(path):
@@ -130,6 +184,19 @@ def main():
               "(this path runs on a single GPU; see DESIGN.md for how it would shard)",
               file=sys.stderr)
         sys.exit(2)
+    if args.record_traffic:
+        from workloads import get_config
+        from workloads.gen import indptr_from_lens
+        import varlen_prefill_amd as vp
+        cfg = get_config(args.workload)
+        causal = cfg.causal and not args.noncausal
+        plan = vp.Plan(indptr_from_lens(cfg.qo_lens), indptr_from_lens(cfg.kv_lens),
+                       cfg.num_qo_heads, cfg.num_kv_heads, cfg.head_dim, causal, host_only=True)
+        path = record_traffic(args.record_traffic[0], args.record_traffic[1],
+                              cfg.name + ("" if causal else "_noncausal"), cfg.head_dim,
+                              plan.info["bytes"])
+        print(path)
+        return
     import torch
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)

@@ -28,8 +28,8 @@ constexpr int kDefaultKvChunk = 8192;
 constexpr int kChunkAlign = 64;     // kv_chunk must be a multiple of this
 constexpr int kDefaultXcds = 8;     // MI355X: 8 XCDs, workgroups dispatched round-robin
 // Key blocks are computed with P split into a bf16 hi part and a bf16 lo
-// remainder when the block is partially masked for the tile or when the
-// tile's first row sees at most this many keys.
+// remainder when the tile's first row sees at most this many keys (and, at
+// head_dim 256, on blocks partially masked for the tile).
 constexpr int kHiLoKeys = 128;
 
 // Key-block shape of the tile kernel: keys per block and LDS pipeline depth

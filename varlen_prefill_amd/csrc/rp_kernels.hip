@@ -14,10 +14,11 @@
 // with transposed products keeps every row's scores inside one lane pair and
 // lets P feed the second MFMA straight from registers.
 //
-// P is rounded to bf16 for the PV MFMA.  On key blocks that are partially
-// masked for the tile, and on every block of tiles whose first row sees at
-// most kHiLoKeys keys, P is split into bf16 hi + bf16 lo (two MFMAs), which
-// keeps rows with few keys accurate to well under one bf16 ulp of O.
+// P is rounded to bf16 for the PV MFMA.  In tiles whose first row sees at
+// most kHiLoKeys keys (and, at head_dim 256, on partially masked blocks),
+// P is split into bf16 hi + bf16 lo (two MFMAs), which keeps rows with few
+// keys accurate to well under one bf16 ulp of O; rows that see more keys
+// average the rounding of P over many terms.
 //
 // merge_kernel: folds the fp32 partial states of split tiles, chunk by chunk
 // in ascending key order (merge of attention states, page
@@ -430,11 +431,23 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
             __syncthreads();
         }
     };
-    if (hilo_all)
-        run(std::false_type{}, std::true_type{}, kb_begin, kb_mask);
-    else
-        run(std::false_type{}, std::false_type{}, kb_begin, kb_mask);
-    run(std::true_type{}, std::true_type{}, kb_mask, kb_end);
+    if constexpr (HD == 128) {
+        if (hilo_all) {
+            run(std::false_type{}, std::true_type{}, kb_begin, kb_mask);
+            run(std::true_type{}, std::true_type{}, kb_mask, kb_end);
+        } else {
+            run(std::false_type{}, std::false_type{}, kb_begin, kb_mask);
+            run(std::true_type{}, std::false_type{}, kb_mask, kb_end);
+        }
+    } else {
+        // head_dim 256 keeps hi/lo on every masked block: one loop variant
+        // less keeps its register allocation free of spills in the loops
+        if (hilo_all)
+            run(std::false_type{}, std::true_type{}, kb_begin, kb_mask);
+        else
+            run(std::false_type{}, std::false_type{}, kb_begin, kb_mask);
+        run(std::true_type{}, std::true_type{}, kb_mask, kb_end);
+    }
 
     // ---- epilogue ----
     const float lt = pair_sum(st.l);

@@ -258,7 +258,7 @@ int build_plan(const int32_t *q_indptr, const int32_t *kv_indptr, const PlanShap
             const int64_t kb1 = (it.key_end + bk - 1) / bk;
             for (int64_t kb = kb0; kb < kb1; ++kb) {
                 const bool mask = (kb + 1) * bk > it.lim_first;
-                const bool hilo = mask || it.lim_first <= kHiLoKeys;
+                const bool hilo = it.lim_first <= kHiLoKeys || (mask && shape.head_dim == 256);
                 cost += hilo ? 3 : 2;
             }
         }
