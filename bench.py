@@ -14,6 +14,9 @@ Default workload: 8 requests, qo_len = kv_len ~ U[128, 2048] (recorded lengths),
 32 qo / 8 kv heads, head_dim 128, causal, bf16 N(0,1) inputs.
 
 Other modes:
+  --paged P            the same batch with K/V scattered into a page pool of
+                       P-key pages in random order; a step is one rp_run_paged
+                       call on a plan built once before the timed region.
   --copy-probe-mib M   run a plain device copy of M MiB (read M, write M) a few
                        times; used to scale rocprofv3 FETCH_SIZE/WRITE_SIZE.
   --record-traffic KDIR CDIR
@@ -60,6 +63,8 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="hd128_gqa_causal")
     p.add_argument("--noncausal", action="store_true", help="run the workload without the causal mask")
+    p.add_argument("--paged", type=int, default=0, metavar="PAGE_SIZE",
+                   help="keep K/V in a paged cache of this page size (rp_run_paged on a prebuilt plan)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle baseline sample")
@@ -207,6 +212,7 @@ def main():
 
     cfg = get_config(args.workload)
     causal = cfg.causal and not args.noncausal
+    workload = cfg.name + ("" if causal else "_noncausal") + (f"_paged{args.paged}" if args.paged else "")
     batch = make_config_batch(cfg)
     sm_scale = float(np.float32(1.0 / math.sqrt(cfg.head_dim)))
     dev = torch.device("cuda:0")
@@ -240,9 +246,25 @@ def main():
                  cfg.num_kv_heads, cfg.head_dim, 1 if causal else 0, ctypes.c_float(sm_scale),
                  ctypes.c_void_p(stream.cuda_stream))
     step = lib.ragged_prefill_bf16
+    step_name = "ragged_prefill_bf16"
+    if args.paged:
+        from workloads import make_paged
+        pk = make_paged(batch, args.paged, seed=cfg.seed)
+        kp, vpg = pk.k_pages.to(dev), pk.v_pages.to(dev)
+        table = torch.from_numpy(pk.block_table).to(dev)
+        paged_plan = vp.Plan(batch.q_indptr, batch.kv_indptr, cfg.num_qo_heads, cfg.num_kv_heads,
+                             cfg.head_dim, causal)
+        ws = torch.empty(max(paged_plan.workspace_bytes, 1), dtype=torch.uint8, device=dev)
+        call_args = (paged_plan.handle, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(kp.data_ptr()),
+                     ctypes.c_void_p(vpg.data_ptr()), ctypes.c_void_p(table.data_ptr()),
+                     int(table.shape[1]), args.paged, ctypes.c_void_p(o.data_ptr()),
+                     ctypes.c_void_p(lse.data_ptr()), ctypes.c_float(sm_scale),
+                     ctypes.c_void_p(ws.data_ptr()), ws.numel(), ctypes.c_void_p(stream.cuda_stream))
+        step = lib.rp_run_paged
+        step_name = "rp_run_paged"
 
     for _ in range(args.warmup):
-        _lib.check(step(*call_args), "ragged_prefill_bf16")
+        _lib.check(step(*call_args), step_name)
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -251,7 +273,7 @@ def main():
     for _ in range(args.steps):
         st = step(*call_args)
         if st != 0:
-            _lib.check(st, "ragged_prefill_bf16")
+            _lib.check(st, step_name)
     ev1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -263,7 +285,7 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (gpu_ms_per_step * 1e-3) / 1e12
     kernel = f"tile_kernel_hd{cfg.head_dim}"
-    traffic = load_traffic(kernel, cfg.name + ("" if causal else "_noncausal"))
+    traffic = load_traffic(kernel, workload)
     result = {
         "metric": METRIC,
         "value": value,
@@ -278,7 +300,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": cfg.name + ("" if causal else "_noncausal"),
+            "workload": workload,
             "requests": cfg.batch,
             "num_qo_heads": cfg.num_qo_heads,
             "num_kv_heads": cfg.num_kv_heads,
@@ -287,6 +309,7 @@ def main():
             "total_q": cfg.total_q,
             "total_kv": cfg.total_kv,
             "seed": cfg.seed,
+            "kv_layout": f"paged, page_size {args.paged}" if args.paged else "ragged",
         },
         "tokens_per_s": cfg.total_q / (ms_per_step * 1e-3),
         "mfma_peak_frac": value / MFMA_BF16_PEAK_TFLOPS,

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define RP_ABI_VERSION 1
+#define RP_ABI_VERSION 2
 
 /* Status codes. */
 enum rp_status {
@@ -167,6 +167,29 @@ int64_t rp_plan_copy_items(const rp_plan *plan, int32_t *dst, int64_t capacity);
 int rp_run(const rp_plan *plan, const void *q, const void *k, const void *v, void *o,
            float *lse, float sm_scale, void *workspace, size_t workspace_bytes,
            void *stream);
+
+/* Run a plan over PAGED K/V (append prefill over a KV cache; paged KV cache
+ * prefill of page "flashinfer-ai/flashinfer", attention API, and the block
+ * tables, page sizes and NHD layout of page "vllm-rlt PR #112", design
+ * notes).  The plan is the same as for rp_run (built from the kv lengths in
+ * kv_indptr; the offsets themselves are not used here).
+ *   k_pages, v_pages: bf16 page pools [num_pages][page_size][num_kv_heads]
+ *     [head_dim], contiguous, 16-byte aligned, device.
+ *   block_table: int32 [batch][max_blocks_per_seq], device: key j of request
+ *     b is slot j % page_size of page block_table[b][j / page_size].  Entries
+ *     are clamped to >= 0 when read, and entries past a request's
+ *     ceil(kv_len / page_size) pages are never read, so padding (-1, 0, stale
+ *     ids) is invisible.  Every entry that is read must name a page inside
+ *     the pools (not checked).
+ *   page_size: 16, 32, 64 or 128 keys.  max_blocks_per_seq must be at least
+ *     ceil(max kv_len / page_size), else RP_EINVAL.
+ * Everything else (q, o, lse, sm_scale, workspace, stream, ordering) is as for
+ * rp_run; results are bit-identical to rp_run on the same keys stored
+ * contiguously. */
+int rp_run_paged(const rp_plan *plan, const void *q, const void *k_pages, const void *v_pages,
+                 const int32_t *block_table, int max_blocks_per_seq, int page_size, void *o,
+                 float *lse, float sm_scale, void *workspace, size_t workspace_bytes,
+                 void *stream);
 
 void rp_plan_destroy(rp_plan *plan);
 

@@ -138,6 +138,32 @@ def ragged_attention(q, k, v, q_indptr: Sequence[int], kv_indptr: Sequence[int],
     return o, lse
 
 
+def paged_kv_gather(k_pages, v_pages, block_table, kv_lens: Sequence[int], page_size: int):
+    """Contiguous K, V (bf16 bit patterns, [sum(kv_lens), Hkv, D]) and kv_indptr
+    from a paged KV cache, by the definition of the paged layout: key j of
+    request b is slot j % page_size of page block_table[b][j // page_size],
+    table entries clamped to >= 0 (the block tables and page sizes of page
+    "vllm-rlt PR #112", design notes; paged KV cache of page
+    "flashinfer-ai/flashinfer", attention API).  Written key by key."""
+    kb, vb = _bits(k_pages), _bits(v_pages)
+    table = np.asarray(block_table, dtype=np.int64)
+    lens = [int(x) for x in kv_lens]
+    total = sum(lens)
+    k = np.empty((total,) + kb.shape[2:], dtype=np.uint16)
+    v = np.empty((total,) + vb.shape[2:], dtype=np.uint16)
+    indptr = np.zeros(len(lens) + 1, dtype=np.int32)
+    row = 0
+    for b, n in enumerate(lens):
+        indptr[b] = row
+        for j in range(n):
+            page = max(int(table[b, j // page_size]), 0)
+            k[row] = kb[page, j % page_size]
+            v[row] = vb[page, j % page_size]
+            row += 1
+    indptr[len(lens)] = row
+    return k, v, indptr
+
+
 def ragged_attention_rows(q, k, v, q_indptr, kv_indptr, num_qo_heads: int, num_kv_heads: int,
                           causal: bool, sm_scale: float, tokens, heads, lib=None
                           ) -> Tuple[np.ndarray, np.ndarray]:

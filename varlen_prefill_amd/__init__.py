@@ -10,6 +10,7 @@ marshals torch tensors (device memory and the current stream) into that ABI.
 Entry points:
   ragged_prefill(q, k, v, q_indptr, kv_indptr, ...)  one-shot (plans are cached)
   Plan(q_indptr, kv_indptr, ...).run(q, k, v, ...)   plan once, run many
+  Plan(...).run_paged(q, k_pages, v_pages, block_table, ...)   K/V in a paged cache
 """
 
 from __future__ import annotations
@@ -181,6 +182,60 @@ class Plan:
                               ctypes.c_void_p(lse.data_ptr()) if lse is not None else None,
                               ctypes.c_float(scale), ws_ptr, ws_bytes, _stream_handle(stream))
         _lib.check(st, "rp_run")
+        return out, lse
+
+    def run_paged(self, q, k_pages, v_pages, block_table, out=None, lse=None,
+                  sm_scale: Optional[float] = None, return_lse: bool = True, workspace=None,
+                  stream=None):
+        """Run over paged K/V: k_pages, v_pages bf16 [num_pages, page_size,
+        num_kv_heads, head_dim]; block_table int32 [batch, max_blocks] on the
+        GPU (key j of request b: page block_table[b, j // page_size], slot
+        j % page_size; negative entries read as page 0)."""
+        import torch
+        rows_q = int(self.q_indptr[-1])
+        _check_tensor(q, "q", rows_q, self.num_qo_heads, self.head_dim)
+        for name, t in (("k_pages", k_pages), ("v_pages", v_pages)):
+            if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dtype != torch.bfloat16:
+                raise TypeError(f"{name} must be a bf16 GPU tensor")
+            if t.dim() != 4 or t.shape[2] != self.num_kv_heads or t.shape[3] != self.head_dim:
+                raise ValueError(f"{name} must be [num_pages, page_size, {self.num_kv_heads}, "
+                                 f"{self.head_dim}], got {tuple(t.shape)}")
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+        if k_pages.shape != v_pages.shape:
+            raise ValueError("k_pages and v_pages must have the same shape")
+        page_size = int(k_pages.shape[1])
+        if (not isinstance(block_table, torch.Tensor) or block_table.device.type != "cuda"
+                or block_table.dtype != torch.int32 or block_table.dim() != 2
+                or block_table.shape[0] != self.batch or not block_table.is_contiguous()):
+            raise ValueError(f"block_table must be a contiguous int32 [{self.batch}, max_blocks] GPU tensor")
+        if out is None:
+            out = torch.empty_like(q)
+        else:
+            _check_tensor(out, "out", rows_q, self.num_qo_heads, self.head_dim)
+        if lse is None and return_lse:
+            lse = torch.empty((q.shape[0], self.num_qo_heads), dtype=torch.float32, device=q.device)
+        if lse is not None:
+            if (lse.dtype != torch.float32 or lse.device != q.device or not lse.is_contiguous()
+                    or tuple(lse.shape[1:]) != (self.num_qo_heads,) or lse.shape[0] < rows_q):
+                raise ValueError("lse must be a contiguous float32 [rows, num_qo_heads] GPU tensor")
+        need = self.workspace_bytes
+        if workspace is None and need > 0:
+            if self._workspace is None or self._workspace.numel() < need:
+                self._workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            workspace = self._workspace
+        ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        scale = _default_scale(self.head_dim) if sm_scale is None else float(sm_scale)
+        st = self._lib.rp_run_paged(self.handle, ctypes.c_void_p(q.data_ptr()),
+                                    ctypes.c_void_p(k_pages.data_ptr()),
+                                    ctypes.c_void_p(v_pages.data_ptr()),
+                                    ctypes.c_void_p(block_table.data_ptr()),
+                                    int(block_table.shape[1]), page_size,
+                                    ctypes.c_void_p(out.data_ptr()),
+                                    ctypes.c_void_p(lse.data_ptr()) if lse is not None else None,
+                                    ctypes.c_float(scale), ws_ptr, ws_bytes, _stream_handle(stream))
+        _lib.check(st, "rp_run_paged")
         return out, lse
 
     def close(self) -> None:

@@ -39,6 +39,7 @@ EXPORTS = [
     "rp_plan_workspace_bytes",
     "rp_plan_copy_items",
     "rp_run",
+    "rp_run_paged",
     "rp_plan_destroy",
 ]
 
@@ -102,6 +103,8 @@ def load():
         lib.rp_plan_copy_items.restype = ctypes.c_int64
         lib.rp_run.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, ctypes.c_size_t, P]
         lib.rp_run.restype = I
+        lib.rp_run_paged.argtypes = [P, P, P, P, P, I, I, P, P, ctypes.c_float, P, ctypes.c_size_t, P]
+        lib.rp_run_paged.restype = I
         lib.rp_plan_destroy.argtypes = [P]
         lib.rp_plan_destroy.restype = None
         _lib = lib

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -166,8 +167,16 @@ int create_plan(const int32_t *q_indptr, const int32_t *kv_indptr, int batch, in
     return RP_OK;
 }
 
+// Paged K/V of one run (null: contiguous ragged K/V).
+struct PagedKV {
+    const int32_t *block_table;
+    int max_blocks;
+    int page_size;
+};
+
 int run_plan(const rp_plan *p, const void *q, const void *k, const void *v, void *o, float *lse,
-             float sm_scale, void *workspace, size_t workspace_bytes, void *stream)
+             float sm_scale, void *workspace, size_t workspace_bytes, void *stream,
+             const PagedKV *paged = nullptr)
 {
     if (p == nullptr)
         return fail(RP_EINVAL, "plan must not be NULL");
@@ -185,6 +194,26 @@ int run_plan(const rp_plan *p, const void *q, const void *k, const void *v, void
     if (!aligned16(q) || !aligned16(o) || !aligned16(k) || !aligned16(v) ||
         (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
         return fail(RP_EINVAL, "q, k, v and o must be 16-byte aligned (lse 4-byte)");
+    int page_shift = 0;
+    if (paged) {
+        const int ps = paged->page_size;
+        if (ps != 16 && ps != 32 && ps != 64 && ps != 128)
+            return fail(RP_EINVAL, "page_size must be 16, 32, 64 or 128");
+        while ((1 << page_shift) < ps)
+            ++page_shift;
+        int64_t max_kv = 0;
+        for (const rp::Item &it : h.items)
+            max_kv = std::max<int64_t>(max_kv, it.kv_len);
+        const int64_t need_blocks = (max_kv + ps - 1) / ps;
+        if (paged->max_blocks < need_blocks)
+            return fail(RP_EINVAL, "max_blocks_per_seq " + std::to_string(paged->max_blocks) +
+                                       " is below the " + std::to_string(need_blocks) +
+                                       " pages the longest request needs");
+        if (max_kv > 0 && paged->block_table == nullptr)
+            return fail(RP_EINVAL, "block_table must not be NULL");
+        if ((reinterpret_cast<uintptr_t>(paged->block_table) & 3u) != 0)
+            return fail(RP_EINVAL, "block_table must be 4-byte aligned");
+    }
     const size_t need = h.workspace_bytes();
     if (need > 0) {
         if (workspace == nullptr || workspace_bytes < need)
@@ -218,9 +247,14 @@ int run_plan(const rp_plan *p, const void *q, const void *k, const void *v, void
     ta.group = h.shape.num_qo_heads / h.shape.num_kv_heads;
     ta.causal = h.shape.causal;
     ta.scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
+    if (paged) {
+        ta.block_table = paged->block_table;
+        ta.max_blocks = paged->max_blocks;
+        ta.page_shift = page_shift;
+    }
     logf(3, "launch tile kernel: D=%d items=%zu merges=%zu scale_log2=%g", h.shape.head_dim,
          h.items.size(), h.merges.size(), (double)ta.scale_log2);
-    int st = rp::launch_tile_kernel(h.shape.head_dim, ta, (int64_t)h.items.size(), stream);
+    int st = rp::launch_tile_kernel(h.shape.head_dim, paged != nullptr, ta, (int64_t)h.items.size(), stream);
     if (st != (int)hipSuccess)
         return hip_fail((hipError_t)st, "tile kernel launch");
     if (!h.merges.empty()) {
@@ -332,6 +366,14 @@ int rp_run(const rp_plan *p, const void *q, const void *k, const void *v, void *
            float sm_scale, void *workspace, size_t workspace_bytes, void *stream)
 {
     return run_plan(p, q, k, v, o, lse, sm_scale, workspace, workspace_bytes, stream);
+}
+
+int rp_run_paged(const rp_plan *p, const void *q, const void *k_pages, const void *v_pages,
+                 const int32_t *block_table, int max_blocks_per_seq, int page_size, void *o,
+                 float *lse, float sm_scale, void *workspace, size_t workspace_bytes, void *stream)
+{
+    PagedKV pk{block_table, max_blocks_per_seq, page_size};
+    return run_plan(p, q, k_pages, v_pages, o, lse, sm_scale, workspace, workspace_bytes, stream, &pk);
 }
 
 void rp_plan_destroy(rp_plan *p) { free_plan(p); }

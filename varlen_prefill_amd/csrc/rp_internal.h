@@ -98,6 +98,12 @@ struct TileArgs {
     int32_t group;         // num_qo_heads / num_kv_heads
     int32_t causal;
     float scale_log2;      // sm_scale * log2(e)
+    // paged K/V (the paged kernel only): k and v are page pools
+    // [pages][page_size][num_kv_heads][head_dim]; key j of request b sits in
+    // page max(block_table[b * max_blocks + j / page_size], 0), slot j % page_size
+    const int32_t *block_table;
+    int32_t max_blocks;
+    int32_t page_shift;    // log2(page_size)
 };
 
 struct MergeArgs {
@@ -111,7 +117,7 @@ struct MergeArgs {
 };
 
 // Host-side launchers (defined in the .hip file).  Return a hipError_t value.
-int launch_tile_kernel(int head_dim, const TileArgs &args, int64_t num_items, void *stream);
+int launch_tile_kernel(int head_dim, bool paged, const TileArgs &args, int64_t num_items, void *stream);
 int launch_merge_kernel(int head_dim, const MergeArgs &args, int64_t num_items, void *stream);
 
 }  // namespace rp

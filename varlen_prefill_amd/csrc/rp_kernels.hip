@@ -284,7 +284,7 @@ __device__ __attribute__((always_inline)) inline void block_step(
             }
 }
 
-template <int HD, bool POS_SCALE>
+template <int HD, bool POS_SCALE, bool PAGED>
 __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
 {
     using T = Tile<HD>;
@@ -315,7 +315,7 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
     const int kb_end = it.key_end > it.key_begin ? (it.key_end + T::BK - 1) / T::BK : kb_begin;
     const bool hilo_all = it.lim_first <= kHiLoKeys;
 
-    const size_t head_off = ((size_t)it.kv_row0 * a.num_kv_heads + it.kv_head) * HD;
+    const size_t head_off = ((size_t)(PAGED ? 0 : it.kv_row0) * a.num_kv_heads + it.kv_head) * HD;
     const __bf16 *kbase = static_cast<const __bf16 *>(a.k) + head_off;
     const __bf16 *vbase = static_cast<const __bf16 *>(a.v) + head_off;
 
@@ -337,14 +337,37 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
     }
     const int kv_stride_i = a.num_kv_heads * HD;
     const unsigned lds_base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
+    // Paged K/V: the rows one load instruction moves (1 KB: 4 rows at
+    // head_dim 128, 2 at 256) are aligned consecutive keys, clamped to the
+    // request's last key, so they lie in one page (page_size >= 16): one
+    // page id per instruction, read one block ahead from the block table
+    // (entries clamped to >= 0, so padding ids stay harmless).
+    constexpr int ROWS_PER_LOAD = 1024 / T::RB;
+    const int32_t *table_row = PAGED ? a.block_table + (size_t)it.request * a.max_blocks : nullptr;
+    const int page_mask = (1 << a.page_shift) - 1;
+    auto page_ids = [&](int kb, int (&pg)[T::NLOAD]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < T::NLOAD; ++i) {
+            const int key0 = min(kb * T::BK + (T::NLOAD * wu + i) * ROWS_PER_LOAD, it.kv_len - 1);
+            pg[i] = max(table_row[key0 >> a.page_shift], 0);
+        }
+    };
+    int pg_next[T::NLOAD];
     auto issue_loads = [&](int kb, int buf) __attribute__((always_inline)) {
-        const size_t blk = (size_t)kb * T::BK * kv_stride_i;
-        const __bf16 *kb_ptr = kbase + blk;
-        const __bf16 *vb_ptr = vbase + blk;
+        const size_t blk = PAGED ? 0 : (size_t)kb * T::BK * kv_stride_i;
         const int last = it.kv_len - 1 - kb * T::BK;
 #pragma unroll
         for (int i = 0; i < T::NLOAD; ++i) {
-            const int row = min(grow_[i], last);
+            int row = min(grow_[i], last);
+            const __bf16 *kb_ptr = kbase + blk;
+            const __bf16 *vb_ptr = vbase + blk;
+            if (PAGED) {
+                // in-page row of this lane's key; page base in the scalar pointer
+                const size_t page_off = ((size_t)pg_next[i] << a.page_shift) * kv_stride_i;
+                kb_ptr += page_off;
+                vb_ptr += page_off;
+                row = (kb * T::BK + row) & page_mask;
+            }
             const unsigned koff = (unsigned)(row * kv_stride_i + kcol[i]) * 2u;
             const unsigned voff = (unsigned)(row * kv_stride_i + vcol[i]) * 2u;
             const unsigned dk = lds_base + (unsigned)(buf * T::STAGE_BYTES + (T::NLOAD * wu + i) * 1024);
@@ -376,8 +399,13 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
     // The first blocks' K/V loads go out before the Q loads so that the
     // latencies overlap.  Block kb lives in stage (kb - kb_begin) % STAGES.
     const int kb_pre = min(kb_begin + T::STAGES - 1, kb_end);
-    for (int kb = kb_begin; kb < kb_pre; ++kb)
+    for (int kb = kb_begin; kb < kb_pre; ++kb) {
+        if (PAGED)
+            page_ids(kb, pg_next);
         issue_loads(kb, kb - kb_begin);
+    }
+    if (PAGED && kb_pre < kb_end)
+        page_ids(kb_pre, pg_next);
 
     WaveState<HD> st;
     {
@@ -420,8 +448,12 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
         constexpr bool HILO = decltype(hilo_tag)::value;
         for (int kb = kb_from; kb < kb_to; ++kb) {
             const int buf = (kb - kb_begin) % T::STAGES;
-            if (kb + T::STAGES - 1 < kb_end)
+            if (kb + T::STAGES - 1 < kb_end) {
                 issue_loads(kb + T::STAGES - 1, (kb + T::STAGES - 1 - kb_begin) % T::STAGES);
+                // the page ids of the block loaded next iteration
+                if (PAGED && kb + T::STAGES < kb_end)
+                    page_ids(kb + T::STAGES, pg_next);
+            }
             const char *Ks = smem + buf * T::STAGE_BYTES;
             const char *Vs = Ks + T::TILE_BYTES;
             const int thr = lim_row - kb * T::BK - 4 * h;
@@ -487,7 +519,7 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
     }
 }
 
-template <int HD>
+template <int HD, bool PAGED>
 __global__ __launch_bounds__(kThreads, HD == 128 ? 2 : 1) void tile_kernel(TileArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -495,9 +527,9 @@ __global__ __launch_bounds__(kThreads, HD == 128 ? 2 : 1) void tile_kernel(TileA
     if (it.n_tok == 0)
         return;  // padding item of the launch order
     if (a.scale_log2 > 0.0f)
-        tile_body<HD, true>(a, it, smem);
+        tile_body<HD, true, PAGED>(a, it, smem);
     else
-        tile_body<HD, false>(a, it, smem);
+        tile_body<HD, false, PAGED>(a, it, smem);
 }
 
 template <int HD>
@@ -539,26 +571,26 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a)
     }
 }
 
-template <int HD>
+template <int HD, bool PAGED>
 int launch_tile(const TileArgs &args, int64_t num_items, hipStream_t stream)
 {
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&tile_kernel<HD>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&tile_kernel<HD, PAGED>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
                                            Tile<HD>::LDS_BYTES);
         if (e != hipSuccess)
             return (int)e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(tile_kernel<HD>, dim3((unsigned)num_items), dim3(kThreads),
+    hipLaunchKernelGGL((tile_kernel<HD, PAGED>), dim3((unsigned)num_items), dim3(kThreads),
                        Tile<HD>::LDS_BYTES, stream, args);
     return (int)hipGetLastError();
 }
 
 }  // namespace
 
-int launch_tile_kernel(int head_dim, const TileArgs &args, int64_t num_items, void *stream)
+int launch_tile_kernel(int head_dim, bool paged, const TileArgs &args, int64_t num_items, void *stream)
 {
     if (num_items <= 0)
         return (int)hipSuccess;
@@ -566,9 +598,9 @@ int launch_tile_kernel(int head_dim, const TileArgs &args, int64_t num_items, vo
         return (int)hipErrorInvalidValue;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (head_dim == 128)
-        return launch_tile<128>(args, num_items, s);
+        return paged ? launch_tile<128, true>(args, num_items, s) : launch_tile<128, false>(args, num_items, s);
     if (head_dim == 256)
-        return launch_tile<256>(args, num_items, s);
+        return paged ? launch_tile<256, true>(args, num_items, s) : launch_tile<256, false>(args, num_items, s);
     return (int)hipErrorInvalidValue;
 }
 

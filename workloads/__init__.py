@@ -12,7 +12,7 @@ Layout (the packed "NHD" layout of the FlashInfer ragged prefill API, page
 """
 
 from .configs import CONFIGS, WorkloadConfig, get_config
-from .gen import RaggedBatch, make_batch, make_config_batch, request_tensors
+from .gen import PagedKV, RaggedBatch, make_batch, make_config_batch, make_paged, request_tensors
 
 __all__ = [
     "CONFIGS",
@@ -22,4 +22,6 @@ __all__ = [
     "make_batch",
     "make_config_batch",
     "request_tensors",
+    "PagedKV",
+    "make_paged",
 ]

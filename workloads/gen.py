@@ -109,3 +109,50 @@ def make_batch(qo_lens: Sequence[int], kv_lens: Sequence[int], num_qo_heads: int
 def make_config_batch(cfg: WorkloadConfig) -> RaggedBatch:
     return make_batch(cfg.qo_lens, cfg.kv_lens, cfg.num_qo_heads, cfg.num_kv_heads,
                       cfg.head_dim, cfg.seed)
+
+
+@dataclass
+class PagedKV:
+    """A batch's K/V scattered into a page pool (NHD pages)."""
+    k_pages: torch.Tensor      # bf16 [num_pages, page_size, Hkv, D] (CPU)
+    v_pages: torch.Tensor      # bf16 [num_pages, page_size, Hkv, D] (CPU)
+    block_table: np.ndarray    # int32 [batch, max_blocks]
+    page_size: int
+
+
+def make_paged(batch: RaggedBatch, page_size: int, seed: int, spare_pages: int = 3,
+               spare_columns: int = 2) -> PagedKV:
+    """Scatter each request's keys into pages of ``page_size`` keys at random
+    physical positions of a pool.
+
+    Logical page p of request b (keys p*page_size ...) goes to physical page
+    ``block_table[b, p]``.  Slots past a request's last key hold NaN, and the
+    pool has ``spare_pages`` pages no request uses (NaN as well).  Table
+    columns past a request's pages hold padding: -1, 0 or a stale id of
+    another page, drawn at random.  None of this padding may change a result.
+    """
+    rng = np.random.default_rng([seed, 7919, page_size])
+    kv_lens = np.diff(batch.kv_indptr).astype(np.int64)
+    need = (kv_lens + page_size - 1) // page_size
+    n_pages = int(need.sum()) + spare_pages
+    perm = rng.permutation(n_pages)
+    hkv, d = batch.num_kv_heads, batch.head_dim
+    kp = torch.full((max(n_pages, 1), page_size, hkv, d), float("nan"), dtype=torch.bfloat16)
+    vp = torch.full((max(n_pages, 1), page_size, hkv, d), float("nan"), dtype=torch.bfloat16)
+    max_blocks = int(need.max() if len(need) else 0) + spare_columns
+    table = np.zeros((batch.batch, max(max_blocks, 1)), dtype=np.int32)
+    nxt = 0
+    for b in range(batch.batch):
+        base = int(batch.kv_indptr[b])
+        for p in range(int(need[b])):
+            phys = int(perm[nxt])
+            nxt += 1
+            table[b, p] = phys
+            lo = p * page_size
+            hi = min(lo + page_size, int(kv_lens[b]))
+            kp[phys, : hi - lo] = batch.k[base + lo: base + hi]
+            vp[phys, : hi - lo] = batch.v[base + lo: base + hi]
+        pad = rng.integers(0, 3, table.shape[1] - int(need[b]))
+        stale = rng.integers(0, max(n_pages, 1), pad.size)
+        table[b, int(need[b]):] = np.where(pad == 0, -1, np.where(pad == 1, 0, stale))
+    return PagedKV(k_pages=kp, v_pages=vp, block_table=table, page_size=page_size)
