@@ -136,7 +136,7 @@ def record_traffic(kdir: str, cdir: str, workload: str, head_dim: int, alg_bytes
         with open(path) as f:
             return [float(r["Counter_Value"]) for r in csv.DictReader(f) if pick(r["Kernel_Name"])]
 
-    tile = lambda name: f"tile_kernel<{head_dim}>" in name
+    tile = lambda name: f"tile_kernel<{head_dim}" in name
     copy = lambda name: "copyBuffer" in name
     fetch = values(os.path.join(kdir, "fetch_counter_collection.csv"), tile)
     write = values(os.path.join(kdir, "write_counter_collection.csv"), tile)
@@ -198,7 +198,8 @@ def main():
         plan = vp.Plan(indptr_from_lens(cfg.qo_lens), indptr_from_lens(cfg.kv_lens),
                        cfg.num_qo_heads, cfg.num_kv_heads, cfg.head_dim, causal, host_only=True)
         path = record_traffic(args.record_traffic[0], args.record_traffic[1],
-                              cfg.name + ("" if causal else "_noncausal"), cfg.head_dim,
+                              cfg.name + ("" if causal else "_noncausal")
+                              + (f"_paged{args.paged}" if args.paged else ""), cfg.head_dim,
                               plan.info["bytes"])
         print(path)
         return

@@ -73,3 +73,26 @@ def test_staging_and_reads_stay_in_bounds(hd):
                     pos = cc ^ swz_v(row)
                     assert 0 <= pos < cpr and row + 8 < bk
                     assert (row + 8) * rb + 16 * pos + 8 * (s16 & 1) + 8 <= tile
+
+
+@pytest.mark.parametrize("hd", [128, 256])
+def test_paged_wave_rows_share_one_page(hd):
+    """The paged loader reads one block-table entry per wave and block, for
+    key kb*BK + w*WAVE_ROWS (clamped to the last key).  That is right only if
+    every row a wave's loads touch lies in the same 16-key-aligned group as
+    that key, also after clamping rows past the request's end."""
+    bk, _ = _shape(hd)
+    threads = 256
+    rb, cpr = hd * 2, hd // 8
+    nload = bk * rb // 1024 // (threads // 64)
+    wave_rows = nload * 1024 // rb
+    assert 16 % wave_rows == 0
+    for w in range(threads // 64):
+        rows = {((nload * w + i) * 64 + lane) // cpr for i in range(nload) for lane in range(64)}
+        assert min(rows) == w * wave_rows and max(rows) < (w + 1) * wave_rows
+        for kb in range(3):
+            for kv_len in range(1, 4 * bk + 1):
+                key0 = min(kb * bk + w * wave_rows, kv_len - 1)
+                for r in rows:
+                    key = kb * bk + min(r, kv_len - 1 - kb * bk)
+                    assert key // 16 == key0 // 16

@@ -325,49 +325,67 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
     // of the request are clamped to its last key: those keys are masked
     // (P = 0 exactly), so the data there is inert.
     const int wu = __builtin_amdgcn_readfirstlane(w);
-    int grow_[T::NLOAD], kcol[T::NLOAD], vcol[T::NLOAD];
-#pragma unroll
-    for (int i = 0; i < T::NLOAD; ++i) {
-        const int chunk = (T::NLOAD * wu + i) * 64 + lane;
+    // Lane offsets of load i.  The paged head_dim 256 kernel recomputes them
+    // at every issue from a fresh lane id (the empty asm keeps the compiler
+    // from hoisting them out of the loop): kept live there, they are spilled,
+    // and the scratch reload after the K/V loads waits for those loads too
+    // (measured: 20 % slower).  The other kernels keep them live, which
+    // measured faster for them.
+    auto lane_offsets = [&](int ln, int i, int &grow, int &kc, int &vc) __attribute__((always_inline)) {
+        const int chunk = (T::NLOAD * wu + i) * 64 + ln;
         const int rr = chunk / T::CPR;
         const int pp = chunk - rr * T::CPR;
-        grow_[i] = rr;
-        kcol[i] = 8 * (pp ^ swz_k(rr));
-        vcol[i] = 8 * (pp ^ swz_v(rr));
+        grow = rr;
+        kc = 8 * (pp ^ swz_k(rr));
+        vc = 8 * (pp ^ swz_v(rr));
+    };
+    constexpr bool KEEP_OFFSETS = HD == 128 || !PAGED;
+    int grow_[T::NLOAD], kcol[T::NLOAD], vcol[T::NLOAD];
+    if constexpr (KEEP_OFFSETS) {
+#pragma unroll
+        for (int i = 0; i < T::NLOAD; ++i)
+            lane_offsets(lane, i, grow_[i], kcol[i], vcol[i]);
     }
     const int kv_stride_i = a.num_kv_heads * HD;
     const unsigned lds_base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
-    // Paged K/V: the rows one load instruction moves (1 KB: 4 rows at
-    // head_dim 128, 2 at 256) are aligned consecutive keys, clamped to the
-    // request's last key, so they lie in one page (page_size >= 16): one
-    // page id per instruction, read one block ahead from the block table
-    // (entries clamped to >= 0, so padding ids stay harmless).
-    constexpr int ROWS_PER_LOAD = 1024 / T::RB;
+    // Paged K/V: a wave's loads of one block move WAVE_ROWS aligned
+    // consecutive keys (clamped to the request's last key), so with pages of
+    // at least 16 keys they lie in one page: one page id per wave and block,
+    // clamped to >= 0 where it is used (padding ids stay harmless).  The id
+    // of block kb + 1 is read with an ordinary vector load issued right after
+    // block kb's K/V loads: loads complete in order, so the vmcnt wait that
+    // ends the iteration covers it and its use at the next issue waits for
+    // nothing.  (A scalar load would share lgkmcnt with the LDS reads and
+    // turn their graduated waits into full ones.)
+    constexpr int WAVE_ROWS = T::NLOAD * 1024 / T::RB;
+    static_assert(16 % WAVE_ROWS == 0, "a wave's rows must lie in one 16-key page");
     const int32_t *table_row = PAGED ? a.block_table + (size_t)it.request * a.max_blocks : nullptr;
     const int page_mask = (1 << a.page_shift) - 1;
-    auto page_ids = [&](int kb, int (&pg)[T::NLOAD]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < T::NLOAD; ++i) {
-            const int key0 = min(kb * T::BK + (T::NLOAD * wu + i) * ROWS_PER_LOAD, it.kv_len - 1);
-            pg[i] = max(table_row[key0 >> a.page_shift], 0);
-        }
+    int pg_next = 0;
+    auto page_id = [&](int kb) __attribute__((always_inline)) {
+        const int key0 = min(kb * T::BK + wu * WAVE_ROWS, it.kv_len - 1);
+        pg_next = table_row[key0 >> a.page_shift];
     };
-    int pg_next[T::NLOAD];
     auto issue_loads = [&](int kb, int buf) __attribute__((always_inline)) {
-        const size_t blk = PAGED ? 0 : (size_t)kb * T::BK * kv_stride_i;
+        // page base (paged) or block base in the scalar pointer
+        const size_t blk = PAGED ? ((size_t)__builtin_amdgcn_readfirstlane(max(pg_next, 0)) << a.page_shift) * kv_stride_i
+                                 : (size_t)kb * T::BK * kv_stride_i;
+        const __bf16 *kb_ptr = kbase + blk;
+        const __bf16 *vb_ptr = vbase + blk;
         const int last = it.kv_len - 1 - kb * T::BK;
+        int ln = lane;
+        if constexpr (!KEEP_OFFSETS) {
+            ln = __lane_id();
+            asm volatile("" : "+v"(ln));
+#pragma unroll
+            for (int i = 0; i < T::NLOAD; ++i)
+                lane_offsets(ln, i, grow_[i], kcol[i], vcol[i]);
+        }
 #pragma unroll
         for (int i = 0; i < T::NLOAD; ++i) {
             int row = min(grow_[i], last);
-            const __bf16 *kb_ptr = kbase + blk;
-            const __bf16 *vb_ptr = vbase + blk;
-            if (PAGED) {
-                // in-page row of this lane's key; page base in the scalar pointer
-                const size_t page_off = ((size_t)pg_next[i] << a.page_shift) * kv_stride_i;
-                kb_ptr += page_off;
-                vb_ptr += page_off;
-                row = (kb * T::BK + row) & page_mask;
-            }
+            if (PAGED)
+                row = (kb * T::BK + row) & page_mask;   // in-page row of this lane's key
             const unsigned koff = (unsigned)(row * kv_stride_i + kcol[i]) * 2u;
             const unsigned voff = (unsigned)(row * kv_stride_i + vcol[i]) * 2u;
             const unsigned dk = lds_base + (unsigned)(buf * T::STAGE_BYTES + (T::NLOAD * wu + i) * 1024);
@@ -401,11 +419,11 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
     const int kb_pre = min(kb_begin + T::STAGES - 1, kb_end);
     for (int kb = kb_begin; kb < kb_pre; ++kb) {
         if (PAGED)
-            page_ids(kb, pg_next);
+            page_id(kb);
         issue_loads(kb, kb - kb_begin);
     }
     if (PAGED && kb_pre < kb_end)
-        page_ids(kb_pre, pg_next);
+        page_id(kb_pre);
 
     WaveState<HD> st;
     {
@@ -452,7 +470,7 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
                 issue_loads(kb + T::STAGES - 1, (kb + T::STAGES - 1 - kb_begin) % T::STAGES);
                 // the page ids of the block loaded next iteration
                 if (PAGED && kb + T::STAGES < kb_end)
-                    page_ids(kb + T::STAGES, pg_next);
+                    page_id(kb + T::STAGES);
             }
             const char *Ks = smem + buf * T::STAGE_BYTES;
             const char *Vs = Ks + T::TILE_BYTES;
