@@ -17,6 +17,12 @@ Other modes:
   --paged P            the same batch with K/V scattered into a page pool of
                        P-key pages in random order; a step is one rp_run_paged
                        call on a plan built once before the timed region.
+  --shared-prefix P    the workload with its first P keys shared by all requests
+                       (SharedPrefixPlan: all queries against the prefix once,
+                       each request against its own keys, state merge), and
+                       the flat run over the same keys for comparison.
+  --merge-states K     the state-merge kernel alone (K states per row-head),
+                       reported in GB/s against the HBM peak.
   --copy-probe-mib M   run a plain device copy of M MiB (read M, write M) a few
                        times; used to scale rocprofv3 FETCH_SIZE/WRITE_SIZE.
   --record-traffic KDIR CDIR
@@ -63,6 +69,12 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="hd128_gqa_causal")
     p.add_argument("--noncausal", action="store_true", help="run the workload without the causal mask")
+    p.add_argument("--shared-prefix", type=int, default=0, metavar="P",
+                   help="the workload's first P keys are one prefix shared by every request: "
+                        "shared-prefix attention (two levels + state merge), timed beside the "
+                        "flat run over the same keys")
+    p.add_argument("--merge-states", type=int, default=0, metavar="K",
+                   help="time rp_merge_states over K states per (token, qo head) of the workload")
     p.add_argument("--paged", type=int, default=0, metavar="PAGE_SIZE",
                    help="keep K/V in a paged cache of this page size (rp_run_paged on a prebuilt plan)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -182,6 +194,135 @@ def load_traffic(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def _time_steps(step, warmup: int, steps: int, stream):
+    """Wall time and HIP-event time (on `stream`) of `steps` calls, ms/step."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return wall, ev0.elapsed_time(ev1) / steps
+
+
+def bench_shared_prefix(args, cfg, causal: bool) -> dict:
+    import torch
+    import varlen_prefill_amd as vp
+    from varlen_prefill_amd import _lib
+    from workloads import make_batch, request_tensors
+    p_len = args.shared_prefix
+    own = [kv - p_len for kv in cfg.kv_lens]
+    if min(own) < 0 or (causal and any(q > k for q, k in zip(cfg.qo_lens, own))):
+        raise SystemExit(f"--shared-prefix {p_len}: every request needs kv_len - P >= qo_len")
+    d, hq, hkv = cfg.head_dim, cfg.num_qo_heads, cfg.num_kv_heads
+    b = make_batch(cfg.qo_lens, own, hq, hkv, d, cfg.seed)
+    _, ks, vs = request_tensors(cfg.seed, 10**6, 0, p_len, hq, hkv, d)
+    sm = float(np.float32(1.0 / math.sqrt(d)))
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    lib = _lib.load()
+    q = b.q.to(dev)
+    ks_d, vs_d, ku, vu = ks.to(dev), vs.to(dev), b.k.to(dev), b.v.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((q.shape[0], hq), dtype=torch.float32, device=dev)
+    sp = vp.SharedPrefixPlan(b.q_indptr, b.kv_indptr, p_len, hq, hkv, d, causal)
+    ws = torch.empty(max(sp.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+    info = sp.info
+    P = ctypes.c_void_p
+    sp_args = (sp.handle, P(q.data_ptr()), P(ks_d.data_ptr()), P(vs_d.data_ptr()), P(ku.data_ptr()),
+               P(vu.data_ptr()), P(o.data_ptr()), P(lse.data_ptr()), ctypes.c_float(sm),
+               P(ws.data_ptr()), ws.numel(), P(stream.cuda_stream))
+
+    def step_sp():
+        _lib.check(lib.rp_run_shared_prefix(*sp_args), "rp_run_shared_prefix")
+    wall, gpu = _time_steps(step_sp, args.warmup, args.steps, stream)
+    # the flat run over the same keys: every request holds its own copy of the prefix
+    kf, vf = [], []
+    for r in range(b.batch):
+        sl = slice(int(b.kv_indptr[r]), int(b.kv_indptr[r + 1]))
+        kf += [ks, b.k[sl]]
+        vf += [vs, b.v[sl]]
+    kf, vf = torch.cat(kf).to(dev), torch.cat(vf).to(dev)
+    flat_kv = np.concatenate([[0], np.cumsum(cfg.kv_lens)]).astype(np.int32)
+    flat = vp.Plan(b.q_indptr, flat_kv, hq, hkv, d, causal)
+    fws = torch.empty(max(flat.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+    of = torch.empty_like(q)
+    f_args = (flat.handle, P(q.data_ptr()), P(kf.data_ptr()), P(vf.data_ptr()), P(of.data_ptr()),
+              P(lse.data_ptr()), ctypes.c_float(sm), P(fws.data_ptr()), fws.numel(),
+              P(stream.cuda_stream))
+
+    def step_flat():
+        _lib.check(lib.rp_run(*f_args), "rp_run")
+    fwall, fgpu = _time_steps(step_flat, args.warmup, args.steps, stream)
+    flops = info["flops"]
+    assert abs(flops - flat.info["flops"]) < 1e-6 * flops
+    value = flops / (wall * 1e-3) / 1e12
+    achieved = flops / (gpu * 1e-3) / 1e12
+    return {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}_shared{p_len}" + ("" if causal else "_noncausal"),
+                   "requests": cfg.batch, "num_qo_heads": hq, "num_kv_heads": hkv,
+                   "head_dim": d, "causal": causal, "shared_kv_len": p_len,
+                   "total_q": cfg.total_q, "own_kv": int(sum(own)), "seed": cfg.seed},
+        "tokens_per_s": cfg.total_q / (wall * 1e-3),
+        "mfma_peak_frac": value / MFMA_BF16_PEAK_TFLOPS,
+        "alg_gflop_per_step": flops / 1e9, "alg_mb_per_step": info["bytes"] / 1e6,
+        "gpu_ms_per_step": gpu,
+        "flat_gpu_ms_per_step": fgpu, "flat_ms_per_step": fwall,
+        "flat_alg_mb_per_step": flat.info["bytes"] / 1e6,
+        "speedup_vs_flat": fgpu / gpu,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "tile_kernel_hd%d (both levels) + merge_kernel + state_merge_kernel" % d},
+        "cpu_baseline": None,
+    }
+
+
+def bench_merge_states(args, cfg) -> dict:
+    import torch
+    import varlen_prefill_amd as vp
+    from varlen_prefill_amd import _lib
+    k, rows, h, d = args.merge_states, cfg.total_q, cfg.num_qo_heads, cfg.head_dim
+    gen = torch.Generator().manual_seed(cfg.seed)
+    dev = torch.device("cuda:0")
+    v = torch.randn((rows, k, h, d), generator=gen).to(torch.bfloat16).to(dev)
+    s = (torch.rand((rows, k, h), generator=gen) * 20 - 10).to(dev)
+    vo = torch.empty((rows, h, d), dtype=torch.bfloat16, device=dev)
+    so = torch.empty((rows, h), dtype=torch.float32, device=dev)
+    lib = _lib.load()
+    stream = torch.cuda.current_stream()
+    P = ctypes.c_void_p
+    a = (P(v.data_ptr()), P(s.data_ptr()), P(vo.data_ptr()), P(so.data_ptr()), rows, k, h, d,
+         P(stream.cuda_stream))
+
+    def step():
+        _lib.check(lib.rp_merge_states(*a), "rp_merge_states")
+    wall, gpu = _time_steps(step, args.warmup, args.steps, stream)
+    nbytes = rows * h * ((k + 1) * (2 * d + 4))       # read k states, write one
+    gbs = nbytes / (gpu * 1e-3) / 1e9
+    return {
+        "metric": "state merge GB/s", "value": nbytes / (wall * 1e-3) / 1e9, "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"merge_states_k{k}_{cfg.name}", "rows": rows, "num_states": k,
+                   "num_heads": h, "head_dim": d},
+        "gpu_ms_per_step": gpu,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "state_merge_kernel"},
+        "cpu_baseline": None,
+    }
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -213,6 +354,13 @@ def main():
 
     cfg = get_config(args.workload)
     causal = cfg.causal and not args.noncausal
+    if args.shared_prefix or args.merge_states:
+        if not vp.available():
+            raise SystemExit("the gfx950 library is not usable on this device")
+        res = (bench_shared_prefix(args, cfg, causal) if args.shared_prefix
+               else bench_merge_states(args, cfg))
+        print(json.dumps(res))
+        return
     workload = cfg.name + ("" if causal else "_noncausal") + (f"_paged{args.paged}" if args.paged else "")
     batch = make_config_batch(cfg)
     sm_scale = float(np.float32(1.0 / math.sqrt(cfg.head_dim)))

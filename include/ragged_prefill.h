@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define RP_ABI_VERSION 2
+#define RP_ABI_VERSION 3
 
 /* Status codes. */
 enum rp_status {
@@ -191,7 +191,73 @@ int rp_run_paged(const rp_plan *plan, const void *q, const void *k_pages, const 
                  float *lse, float sm_scale, void *workspace, size_t workspace_bytes,
                  void *stream);
 
+/* Destroys a plan of either kind (a shared-prefix plan frees both levels). */
 void rp_plan_destroy(rp_plan *plan);
+
+/* ---- Attention states and shared-prefix (cascade) attention ----------------
+ * An attention state of a query row and qo head over a key set is (v, s): v
+ * the softmax-weighted mean of the values over that set (bf16 [head_dim]),
+ * s the natural-log log-sum-exp of its scores (fp32), i.e. exactly the O and
+ * LSE that rp_run returns.  States over disjoint key sets merge into the state
+ * over their union (page "flashinfer-ai/flashinfer", cascade API, Merge
+ * Attention States):
+ *     s = log(sum_i exp(s_i)),   v = sum_i exp(s_i - s) v_i,
+ * computed in fp32 in ascending state order, v rounded to bf16 (RNE) once.
+ * A state with s = -inf (empty key set) contributes nothing; if every state
+ * is empty the result is v = +0, s = -inf.
+ * Layouts are contiguous, device memory, v pointers 16-byte aligned:
+ *   v: bf16 [rows][num_heads][head_dim], s: fp32 [rows][num_heads];
+ *   head_dim a power of two in [8, 512]; num_heads in [1, 65535].
+ * s_out may be NULL (LSE not wanted).  Inputs and outputs may alias exactly
+ * (same pointer) but must not otherwise overlap.  Enqueued on `stream`;
+ * rows == 0 returns RP_OK without launching. */
+int rp_merge_state(const void *v_a, const float *s_a, const void *v_b, const float *s_b,
+                   void *v_out, float *s_out, int64_t rows, int num_heads, int head_dim,
+                   void *stream);
+
+/* (v, s) <- merge((v, s), (v_other, s_other)), in place. */
+int rp_merge_state_in_place(void *v, float *s, const void *v_other, const float *s_other,
+                            int64_t rows, int num_heads, int head_dim, void *stream);
+
+/* Merge num_states (>= 1) states per row: v bf16 [rows][num_states][num_heads]
+ * [head_dim], s fp32 [rows][num_states][num_heads] -> v_out bf16 [rows]
+ * [num_heads][head_dim], s_out fp32 [rows][num_heads] (may be NULL). */
+int rp_merge_states(const void *v, const float *s, void *v_out, float *s_out, int64_t rows,
+                    int num_states, int num_heads, int head_dim, void *stream);
+
+/* Shared-prefix attention (cascade attention over a two-level KV cache, page
+ * "flashinfer-ai/flashinfer", cascade API, Cascade Attention; hierarchical KV
+ * for shared prefixes, its feature list): every request of the batch attends
+ * to the same shared_kv_len keys first, then to its own keys
+ * kv_indptr[b]..kv_indptr[b+1].  The result equals attention over the
+ * concatenation [shared keys, own keys] (with the causal mask, bottom-right
+ * aligned, over that concatenation), up to rounding: it is computed as
+ *   1. all query rows q_indptr[0]..q_indptr[batch] against the shared keys
+ *      (one request, no mask) -> a bf16/fp32 state in the workspace,
+ *   2. the ragged batch against the own keys (as rp_run) -> o,
+ *   3. o, lse <- merge of the two states (rp_merge_state), in place.
+ * So the shared K/V are read for all requests at once rather than once per
+ * request, and the intermediate state is rounded to bf16 before the merge.
+ * causal requires qo_len <= kv_len (own keys) in every request when
+ * shared_kv_len > 0 (so that every row sees the whole prefix), else
+ * RP_EINVAL.  The plan is used with rp_run_shared_prefix only (rp_run and
+ * rp_run_paged reject it); rp_plan_get_info reports both levels (flops,
+ * items; bytes add the shared K/V once) and rp_plan_workspace_bytes the whole
+ * workspace. */
+int rp_plan_create_shared_prefix(const int32_t *q_indptr, const int32_t *kv_indptr, int batch,
+                                 int shared_kv_len, int num_qo_heads, int num_kv_heads,
+                                 int head_dim, int causal, const rp_plan_opts *opts,
+                                 rp_plan **out);
+
+/* Run a shared-prefix plan.  k_shared, v_shared: bf16 [shared_kv_len]
+ * [num_kv_heads][head_dim]; k_unique, v_unique: bf16 ragged per kv_indptr;
+ * q, o, lse as for rp_run (lse may be NULL).  workspace: at least
+ * rp_plan_workspace_bytes(plan) bytes, 256-byte aligned (never NULL: it holds
+ * the shared-level state). */
+int rp_run_shared_prefix(const rp_plan *plan, const void *q, const void *k_shared,
+                         const void *v_shared, const void *k_unique, const void *v_unique,
+                         void *o, float *lse, float sm_scale, void *workspace,
+                         size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

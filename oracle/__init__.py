@@ -62,6 +62,8 @@ def _bind(lib):
     lib.oracle_ragged_attention_rows.restype = ctypes.c_int
     lib.oracle_merge_state.argtypes = [P, P, P, P, P, P, ctypes.c_int64, ctypes.c_int]
     lib.oracle_merge_state.restype = None
+    lib.oracle_merge_states.argtypes = [P, P, P, P, ctypes.c_int64, ctypes.c_int, ctypes.c_int]
+    lib.oracle_merge_states.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
@@ -205,6 +207,22 @@ def merge_state(o_a, lse_a, o_b, lse_b, lib=None) -> Tuple[np.ndarray, np.ndarra
     lib.oracle_merge_state(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(o), _ptr(lse),
                            n, d)
     return o, lse
+
+
+def merge_states(o, lse, lib=None) -> Tuple[np.ndarray, np.ndarray]:
+    """Merge k states per row over disjoint key sets (fp64): o [..., k, D],
+    lse [..., k] -> o [..., D], lse [...].  Inputs are widened to fp64."""
+    lib = lib or _load()
+    o = np.ascontiguousarray(o, dtype=np.float64)
+    lse = np.ascontiguousarray(lse, dtype=np.float64)
+    if o.shape[:-1] != lse.shape or o.ndim < 2:
+        raise ValueError("shape mismatch")
+    k, d = o.shape[-2], o.shape[-1]
+    n = int(np.prod(lse.shape[:-1]))
+    out = np.empty(lse.shape[:-1] + (d,), dtype=np.float64)
+    out_lse = np.empty(lse.shape[:-1], dtype=np.float64)
+    lib.oracle_merge_states(_ptr(o), _ptr(lse), _ptr(out), _ptr(out_lse), n, k, d)
+    return out, out_lse
 
 
 def num_threads() -> int:

@@ -269,6 +269,47 @@ void oracle_merge_state(const double *o_a, const double *lse_a, const double *o_
     }
 }
 
+/*
+ * Merge k attention states per row over pairwise disjoint key sets (the
+ * merge_states operation of the same cascade API section).  By the
+ * definition of the state, over the union of the k sets
+ *   lse = log(sum_i exp(lse_i))
+ *   o   = sum_i exp(lse_i - lse) * o_i,
+ * with exp(lse_i - lse) the share of state i's softmax mass.  The largest
+ * lse_i is factored out of the sum (exact in real arithmetic).  Empty states
+ * (lse_i = -inf) carry no mass; if all are empty, o = 0 and lse = -inf.
+ * o: double [n, k, head_dim]; lse: double [n, k]; out: [n, head_dim], [n].
+ */
+void oracle_merge_states(const double *o, const double *lse, double *o_out, double *lse_out,
+                         int64_t n, int k, int head_dim)
+{
+    for (int64_t r = 0; r < n; ++r) {
+        const double *l = lse + r * (int64_t)k;
+        double *vo = o_out + r * (int64_t)head_dim;
+        double m = -INFINITY;
+        for (int i = 0; i < k; ++i)
+            if (l[i] > m)
+                m = l[i];
+        for (int d = 0; d < head_dim; ++d)
+            vo[d] = 0.0;
+        if (m == -INFINITY) {
+            lse_out[r] = -INFINITY;
+            continue;
+        }
+        double total = 0.0;
+        for (int i = 0; i < k; ++i)
+            total += exp(l[i] - m);
+        const double merged = m + log(total);
+        for (int i = 0; i < k; ++i) {
+            const double w = exp(l[i] - merged);
+            const double *vi = o + (r * (int64_t)k + i) * head_dim;
+            for (int d = 0; d < head_dim; ++d)
+                vo[d] += w * vi[d];
+        }
+        lse_out[r] = merged;
+    }
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

@@ -281,6 +281,51 @@ def pin_merge(lib=None):
     np.testing.assert_allclose(ml, l0 + math.log(2.0), rtol=0, atol=1e-15)
 
 
+def pin_merge_states(lib=None):
+    """merge_states over k disjoint key windows equals attention over their
+    union; closed-form weights; identity, order and empty-state cases."""
+    d = 32
+    b = make_batch([9, 30, 4], [9, 64, 40], 4, 2, d, seed=37)
+    for causal in (False, True):
+        full_o, full_l = oracle.ragged_attention(b.q, b.k, b.v, b.q_indptr, b.kv_indptr, 4, 2,
+                                                 causal, SM, lib=lib)
+        for cuts in ((0, 3, 20, -1), (0, 1, 2, 30, 50, -1), (0, 7, 7, -1)):
+            parts = [oracle.ragged_attention(b.q, b.k, b.v, b.q_indptr, b.kv_indptr, 4, 2, causal,
+                                             SM, key_window=(lo, hi), lib=lib)
+                     for lo, hi in zip(cuts[:-1], cuts[1:])]
+            o = np.stack([p[0] for p in parts], axis=-2)    # [rows, Hq, k, D]
+            l = np.stack([p[1] for p in parts], axis=-1)    # [rows, Hq, k]
+            mo, ml = oracle.merge_states(o, l, lib=lib)
+            np.testing.assert_allclose(mo, full_o, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(ml, full_l, rtol=0, atol=1e-12)
+            # the order of the states does not matter
+            perm = np.random.default_rng(len(cuts)).permutation(len(parts))
+            po, pl = oracle.merge_states(o[..., perm, :], l[..., perm], lib=lib)
+            np.testing.assert_allclose(po, mo, rtol=0, atol=1e-14)
+            np.testing.assert_allclose(pl, ml, rtol=0, atol=1e-14)
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((2, 3, d))
+    # closed form: masses 1 : 2 : 5 give weights 1/8, 2/8, 5/8 and lse log 8 (+ offset)
+    for off in (0.0, 40.0, -700.0):
+        l = np.full((2, 3), off) + np.log([1.0, 2.0, 5.0])
+        mo, ml = oracle.merge_states(x, l, lib=lib)
+        np.testing.assert_allclose(mo, (x[:, 0] + 2 * x[:, 1] + 5 * x[:, 2]) / 8, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(ml, off + math.log(8.0), rtol=0, atol=1e-12)
+    # one state is returned unchanged; empty states carry no mass; all empty -> (0, -inf)
+    mo, ml = oracle.merge_states(x[:, :1], np.array([[0.5], [-2.0]]), lib=lib)
+    assert np.array_equal(mo, x[:, 0]) and np.array_equal(ml, [0.5, -2.0])
+    l = np.array([[-np.inf, 1.5, -np.inf], [-np.inf, -np.inf, -np.inf]])
+    mo, ml = oracle.merge_states(x, l, lib=lib)
+    assert np.array_equal(mo[0], x[0, 1]) and ml[0] == 1.5
+    assert np.array_equal(mo[1], np.zeros(d)) and ml[1] == -np.inf
+    # two states: the same as the pairwise merge
+    l2 = np.array([[0.3, -1.2], [4.0, 4.5]])
+    mo, ml = oracle.merge_states(x[:, :2], l2, lib=lib)
+    po, pl = oracle.merge_state(x[:, 0], l2[:, 0], x[:, 1], l2[:, 1], lib=lib)
+    np.testing.assert_allclose(mo, po, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(ml, pl, rtol=0, atol=1e-15)
+
+
 def pin_rows_api(lib=None):
     d = 32
     b = make_batch([9, 30, 0, 4], [12, 64, 3, 40], 4, 2, d, seed=41)
@@ -302,5 +347,6 @@ ALL_PINS = [
     pin_closed_forms,
     pin_invariants,
     pin_merge,
+    pin_merge_states,
     pin_rows_api,
 ]

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = _lib.load()
-    assert lib.rp_abi_version() == 2
+    assert lib.rp_abi_version() == 3
     for st in (0, -1, -2, -3, -4):
         assert lib.rp_status_string(st)
     assert lib.rp_status_string(12345) == b"unknown status"
@@ -110,3 +110,49 @@ def test_run_rejects_host_only_plan():
     assert b"host-only" in lib.rp_last_error()
     st = lib.rp_run(None, None, None, None, None, None, ctypes.c_float(0.1), None, 0, None)
     assert st == _lib.RP_EINVAL
+
+
+def test_merge_entry_points_validate_before_any_launch():
+    lib = _lib.load()
+    P = ctypes.c_void_p
+    buf = (ctypes.c_char * 4096)()
+    p = ctypes.cast(buf, P)
+    # head_dim must be a power of two in [8, 512]
+    for d in (0, 4, 96, 1024):
+        assert lib.rp_merge_state(p, p, p, p, p, p, 4, 2, d, None) == -1
+        assert lib.rp_merge_states(p, p, p, p, 4, 2, 2, d, None) == -1
+    assert lib.rp_merge_states(p, p, p, p, 4, 0, 2, 128, None) == -1      # num_states >= 1
+    assert lib.rp_merge_state(p, p, p, p, p, p, -1, 2, 128, None) == -1   # rows >= 0
+    assert lib.rp_merge_state(None, None, None, None, None, None, 0, 2, 128, None) == 0  # no rows
+    assert lib.rp_merge_state(None, p, p, p, p, p, 3, 2, 128, None) == -1
+    assert lib.rp_merge_state_in_place(p, None, p, p, 3, 2, 128, None) == -1
+
+
+def test_shared_prefix_plan_host_logic():
+    qo, kv, p_len = [30, 130, 0, 7], [30, 200, 9, 7], 700
+    qi = np.concatenate([[5], 5 + np.cumsum(qo)]).astype(np.int32)
+    ki = np.concatenate([[0], np.cumsum(kv)]).astype(np.int32)
+    sp = vp.SharedPrefixPlan(qi, ki, p_len, 32, 8, 128, causal=True, host_only=True)
+    unique = vp.Plan(qi, ki, 32, 8, 128, causal=True, host_only=True)
+    shared = vp.Plan([0, sum(qo)], [0, p_len], 32, 8, 128, causal=False, host_only=True)
+    i_sp, i_u, i_s = sp.info, unique.info, shared.info
+    assert i_sp["num_items"] == i_u["num_items"] + i_s["num_items"]
+    assert i_sp["flops"] == i_u["flops"] + i_s["flops"]
+    assert i_sp["total_kv"] == sum(kv) + p_len
+    # algorithmic bytes add the shared K and V once
+    assert i_sp["bytes"] == i_u["bytes"] + 2 * 2 * p_len * 8 * 128
+    # workspace: level workspace, shared O (bf16) and LSE, own-level LSE over rows [0, q_end)
+    rows = sum(qo)
+    al = lambda x: (x + 255) // 256 * 256
+    need = (al(max(i_u["workspace_bytes"], i_s["workspace_bytes"])) + al(rows * 32 * 128 * 2)
+            + al(rows * 32 * 4) + al(int(qi[-1]) * 32 * 4))
+    assert sp.workspace_bytes == need
+    for x in (sp, unique, shared):
+        x.close()
+    # causal needs qo_len <= kv_len in every request once the prefix is non-empty
+    with pytest.raises(vp.RaggedPrefillError, match="qo_len <= kv_len"):
+        vp.SharedPrefixPlan([0, 10], [0, 5], 1, 4, 2, 128, causal=True, host_only=True)
+    vp.SharedPrefixPlan([0, 10], [0, 5], 0, 4, 2, 128, causal=True, host_only=True).close()
+    vp.SharedPrefixPlan([0, 10], [0, 5], 1, 4, 2, 128, causal=False, host_only=True).close()
+    with pytest.raises(vp.RaggedPrefillError):
+        vp.SharedPrefixPlan([0, 10], [0, 5], -1, 4, 2, 128, causal=False, host_only=True)

@@ -29,6 +29,12 @@ MUTANTS = {
     "merge_swapped_weights": ("vo[d] = va[d] * wa + vb[d] * wb;",
                               "vo[d] = va[d] * wb + vb[d] * wa;"),
     "merge_lse_max_only": ("double lse = m + log(exp(a - m) + exp(b - m));", "double lse = m;"),
+    "merge_states_unnormalised": ("const double w = exp(l[i] - merged);",
+                                  "const double w = exp(l[i] - m);"),
+    "merge_states_lse_no_shift": ("const double merged = m + log(total);",
+                                  "const double merged = log(total);"),
+    "merge_states_first_only": ("for (int i = 0; i < k; ++i)\n            total += exp(l[i] - m);",
+                                "for (int i = 0; i < 1; ++i)\n            total += exp(l[i] - m);"),
     "window_low_ignored": ("int64_t j_lo = key_lo > 0 ? key_lo : 0;", "int64_t j_lo = 0;"),
     "masked_row_nan": ("        *lse_out = -INFINITY;\n        return;",
                        "        *lse_out = NAN;\n        return;"),

@@ -11,6 +11,9 @@ Entry points:
   ragged_prefill(q, k, v, q_indptr, kv_indptr, ...)  one-shot (plans are cached)
   Plan(q_indptr, kv_indptr, ...).run(q, k, v, ...)   plan once, run many
   Plan(...).run_paged(q, k_pages, v_pages, block_table, ...)   K/V in a paged cache
+  SharedPrefixPlan(q_indptr, kv_indptr, shared_kv_len, ...).run(q, k_shared, v_shared,
+                   k_unique, v_unique, ...)            shared-prefix (cascade) attention
+  merge_state / merge_state_in_place / merge_states    merging attention states (v, lse)
 """
 
 from __future__ import annotations
@@ -29,6 +32,10 @@ __all__ = [
     "available",
     "ragged_prefill",
     "Plan",
+    "SharedPrefixPlan",
+    "merge_state",
+    "merge_state_in_place",
+    "merge_states",
     "RaggedPrefillError",
     "RP_SPLIT_AUTO",
     "RP_SPLIT_NEVER",
@@ -249,6 +256,166 @@ class Plan:
             self.close()
         except Exception:
             pass
+
+
+class SharedPrefixPlan(Plan):
+    """Shared-prefix attention: every request attends to ``shared_kv_len``
+    shared keys and then to its own keys ``kv_indptr[b]:kv_indptr[b+1]``
+    (two levels plus a state merge, all in the library; see
+    rp_plan_create_shared_prefix)."""
+
+    def __init__(self, q_indptr, kv_indptr, shared_kv_len: int, num_qo_heads: int,
+                 num_kv_heads: int, head_dim: int, causal: bool = True, kv_chunk: int = 0,
+                 split_mode: int = RP_SPLIT_AUTO, host_only: bool = False, num_xcds: int = 0):
+        lib = _lib.load()
+        self._lib = lib
+        self.q_indptr = _host_indptr(q_indptr)
+        self.kv_indptr = _host_indptr(kv_indptr)
+        if self.q_indptr.shape != self.kv_indptr.shape or self.q_indptr.ndim != 1 or self.q_indptr.size < 1:
+            raise ValueError("q_indptr and kv_indptr must be 1-D with the same length >= 1")
+        self.batch = int(self.q_indptr.size - 1)
+        self.shared_kv_len = int(shared_kv_len)
+        self.num_qo_heads = int(num_qo_heads)
+        self.num_kv_heads = int(num_kv_heads)
+        self.head_dim = int(head_dim)
+        self.causal = bool(causal)
+        opts = RpPlanOpts(int(kv_chunk), int(split_mode), 1 if host_only else 0, int(num_xcds))
+        handle = ctypes.c_void_p()
+        self._handle = None
+        st = lib.rp_plan_create_shared_prefix(_ptr(self.q_indptr), _ptr(self.kv_indptr), self.batch,
+                                              self.shared_kv_len, self.num_qo_heads,
+                                              self.num_kv_heads, self.head_dim,
+                                              1 if self.causal else 0, ctypes.byref(opts),
+                                              ctypes.byref(handle))
+        _lib.check(st, "rp_plan_create_shared_prefix")
+        self._handle = handle
+        self._workspace = None
+
+    def run(self, q, k_shared, v_shared, k_unique, v_unique, out=None, lse=None,
+            sm_scale: Optional[float] = None, return_lse: bool = True, workspace=None,
+            stream=None):
+        import torch
+        rows_q = int(self.q_indptr[-1])
+        _check_tensor(q, "q", rows_q, self.num_qo_heads, self.head_dim)
+        _check_tensor(k_shared, "k_shared", self.shared_kv_len, self.num_kv_heads, self.head_dim)
+        _check_tensor(v_shared, "v_shared", self.shared_kv_len, self.num_kv_heads, self.head_dim)
+        _check_tensor(k_unique, "k_unique", int(self.kv_indptr[-1]), self.num_kv_heads, self.head_dim)
+        _check_tensor(v_unique, "v_unique", int(self.kv_indptr[-1]), self.num_kv_heads, self.head_dim)
+        if out is None:
+            out = torch.empty_like(q)
+        else:
+            _check_tensor(out, "out", rows_q, self.num_qo_heads, self.head_dim)
+        if lse is None and return_lse:
+            lse = torch.empty((q.shape[0], self.num_qo_heads), dtype=torch.float32, device=q.device)
+        if lse is not None:
+            _check_lse(lse, rows_q, self.num_qo_heads, q.device)
+        need = self.workspace_bytes
+        if workspace is None and need > 0:
+            if self._workspace is None or self._workspace.numel() < need:
+                self._workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            workspace = self._workspace
+        ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        scale = _default_scale(self.head_dim) if sm_scale is None else float(sm_scale)
+        st = self._lib.rp_run_shared_prefix(
+            self.handle, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_shared.data_ptr()),
+            ctypes.c_void_p(v_shared.data_ptr()), ctypes.c_void_p(k_unique.data_ptr()),
+            ctypes.c_void_p(v_unique.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+            ctypes.c_void_p(lse.data_ptr()) if lse is not None else None, ctypes.c_float(scale),
+            ws_ptr, ws_bytes, _stream_handle(stream))
+        _lib.check(st, "rp_run_shared_prefix")
+        return out, lse
+
+    def run_paged(self, *args, **kwargs):
+        raise RaggedPrefillError(-1, "a shared-prefix plan runs through run()")
+
+
+def _check_lse(t, rows: int, heads: int, device, name: str = "lse") -> None:
+    import torch
+    if (not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.device != device
+            or not t.is_contiguous() or t.dim() != 2 or t.shape[1] != heads or t.shape[0] < rows):
+        raise ValueError(f"{name} must be a contiguous float32 [rows, {heads}] GPU tensor")
+
+
+def _check_state(v, s, name: str):
+    import torch
+    if not isinstance(v, torch.Tensor) or v.device.type != "cuda" or v.dtype != torch.bfloat16:
+        raise TypeError(f"{name}: v must be a bf16 GPU tensor")
+    if v.dim() != 3 or not v.is_contiguous():
+        raise ValueError(f"{name}: v must be a contiguous [rows, num_heads, head_dim] tensor")
+    _check_lse(s, int(v.shape[0]), int(v.shape[1]), v.device, name=f"{name}: s")
+    if s.shape[0] != v.shape[0]:
+        raise ValueError(f"{name}: s must have {v.shape[0]} rows")
+
+
+def merge_state(v_a, s_a, v_b, s_b, v_out=None, s_out=None, stream=None):
+    """Merge two attention states over disjoint key sets: v bf16 [rows, H, D],
+    s fp32 natural-log LSE [rows, H].  Returns (v, s)."""
+    import torch
+    lib = _lib.load()
+    _check_state(v_a, s_a, "a")
+    _check_state(v_b, s_b, "b")
+    if v_a.shape != v_b.shape:
+        raise ValueError("the two states differ in shape")
+    if v_out is None:
+        v_out = torch.empty_like(v_a)
+    elif v_out.shape != v_a.shape or v_out.dtype != torch.bfloat16 or not v_out.is_contiguous():
+        raise ValueError("v_out must be a contiguous bf16 tensor shaped like v_a")
+    if s_out is None:
+        s_out = torch.empty_like(s_a)
+    else:
+        _check_lse(s_out, int(v_a.shape[0]), int(v_a.shape[1]), v_a.device, "s_out")
+    rows, h, d = (int(x) for x in v_a.shape)
+    st = lib.rp_merge_state(ctypes.c_void_p(v_a.data_ptr()), ctypes.c_void_p(s_a.data_ptr()),
+                            ctypes.c_void_p(v_b.data_ptr()), ctypes.c_void_p(s_b.data_ptr()),
+                            ctypes.c_void_p(v_out.data_ptr()), ctypes.c_void_p(s_out.data_ptr()),
+                            rows, h, d, _stream_handle(stream))
+    _lib.check(st, "rp_merge_state")
+    return v_out, s_out
+
+
+def merge_state_in_place(v, s, v_other, s_other, stream=None):
+    """(v, s) <- merge((v, s), (v_other, s_other))."""
+    lib = _lib.load()
+    _check_state(v, s, "v")
+    _check_state(v_other, s_other, "other")
+    if v.shape != v_other.shape:
+        raise ValueError("the two states differ in shape")
+    rows, h, d = (int(x) for x in v.shape)
+    st = lib.rp_merge_state_in_place(ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(s.data_ptr()),
+                                     ctypes.c_void_p(v_other.data_ptr()),
+                                     ctypes.c_void_p(s_other.data_ptr()), rows, h, d,
+                                     _stream_handle(stream))
+    _lib.check(st, "rp_merge_state_in_place")
+    return v, s
+
+
+def merge_states(v, s, v_out=None, s_out=None, stream=None):
+    """Merge K states per row: v bf16 [rows, K, H, D], s fp32 [rows, K, H] ->
+    (v bf16 [rows, H, D], s fp32 [rows, H])."""
+    import torch
+    lib = _lib.load()
+    if not isinstance(v, torch.Tensor) or v.device.type != "cuda" or v.dtype != torch.bfloat16:
+        raise TypeError("v must be a bf16 GPU tensor")
+    if v.dim() != 4 or not v.is_contiguous():
+        raise ValueError("v must be a contiguous [rows, num_states, num_heads, head_dim] tensor")
+    rows, k, h, d = (int(x) for x in v.shape)
+    if (not isinstance(s, torch.Tensor) or s.dtype != torch.float32 or s.device != v.device
+            or not s.is_contiguous() or tuple(s.shape) != (rows, k, h)):
+        raise ValueError("s must be a contiguous float32 [rows, num_states, num_heads] tensor")
+    if v_out is None:
+        v_out = torch.empty((rows, h, d), dtype=torch.bfloat16, device=v.device)
+    elif tuple(v_out.shape) != (rows, h, d) or v_out.dtype != torch.bfloat16 or not v_out.is_contiguous():
+        raise ValueError("v_out must be a contiguous bf16 [rows, num_heads, head_dim] tensor")
+    if s_out is None:
+        s_out = torch.empty((rows, h), dtype=torch.float32, device=v.device)
+    else:
+        _check_lse(s_out, rows, h, v.device, "s_out")
+    st = lib.rp_merge_states(ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(s.data_ptr()),
+                             ctypes.c_void_p(v_out.data_ptr()), ctypes.c_void_p(s_out.data_ptr()),
+                             rows, k, h, d, _stream_handle(stream))
+    _lib.check(st, "rp_merge_states")
+    return v_out, s_out
 
 
 def ragged_prefill(q, k, v, q_indptr, kv_indptr, causal: bool = True,

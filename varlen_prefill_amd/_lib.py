@@ -41,6 +41,11 @@ EXPORTS = [
     "rp_run",
     "rp_run_paged",
     "rp_plan_destroy",
+    "rp_merge_state",
+    "rp_merge_state_in_place",
+    "rp_merge_states",
+    "rp_plan_create_shared_prefix",
+    "rp_run_shared_prefix",
 ]
 
 
@@ -107,6 +112,19 @@ def load():
         lib.rp_run_paged.restype = I
         lib.rp_plan_destroy.argtypes = [P]
         lib.rp_plan_destroy.restype = None
+        I64 = ctypes.c_int64
+        lib.rp_merge_state.argtypes = [P, P, P, P, P, P, I64, I, I, P]
+        lib.rp_merge_state.restype = I
+        lib.rp_merge_state_in_place.argtypes = [P, P, P, P, I64, I, I, P]
+        lib.rp_merge_state_in_place.restype = I
+        lib.rp_merge_states.argtypes = [P, P, P, P, I64, I, I, I, P]
+        lib.rp_merge_states.restype = I
+        lib.rp_plan_create_shared_prefix.argtypes = [P, P, I, I, I, I, I, I,
+                                                     ctypes.POINTER(RpPlanOpts), ctypes.POINTER(P)]
+        lib.rp_plan_create_shared_prefix.restype = I
+        lib.rp_run_shared_prefix.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_float, P,
+                                             ctypes.c_size_t, P]
+        lib.rp_run_shared_prefix.restype = I
         _lib = lib
         return lib
 

@@ -18,6 +18,7 @@
 
 #include "rp_internal.h"
 #include "rp_plan.h"
+#include "rp_state_merge.h"
 
 struct rp_plan {
     rp::HostPlan host;
@@ -25,6 +26,10 @@ struct rp_plan {
     rp::Item *d_items = nullptr;
     rp::MergeItem *d_merges = nullptr;
     bool host_only = false;
+    // Shared-prefix plans: `host` is the per-request (unique) level and
+    // `shared` the level of all query rows against the shared prefix.
+    rp_plan *shared = nullptr;
+    int64_t q_begin = 0, q_end = 0;  // query rows both levels cover
 };
 
 namespace {
@@ -112,6 +117,7 @@ void free_plan(rp_plan *p)
 {
     if (p == nullptr)
         return;
+    free_plan(p->shared);
     if (p->d_items)
         (void)hipFree(p->d_items);
     if (p->d_merges)
@@ -167,6 +173,53 @@ int create_plan(const int32_t *q_indptr, const int32_t *kv_indptr, int batch, in
     return RP_OK;
 }
 
+// Workspace layout of a shared-prefix plan (offsets in bytes, 256-aligned):
+// [level workspace: max of both levels] [shared-level O, bf16 rows x Hq x D]
+// [shared-level LSE, fp32 rows x Hq] [unique-level LSE, fp32 q_end x Hq].
+struct SharedLayout {
+    size_t o_shared, lse_shared, lse_unique, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+SharedLayout shared_layout(const rp_plan *p)
+{
+    const rp::PlanShape &sh = p->host.shape;
+    const size_t rows = (size_t)(p->q_end - p->q_begin);
+    SharedLayout L;
+    const size_t level = std::max(p->host.workspace_bytes(), p->shared->host.workspace_bytes());
+    L.o_shared = align256(level);
+    L.lse_shared = L.o_shared + align256(rows * sh.num_qo_heads * sh.head_dim * 2);
+    L.lse_unique = L.lse_shared + align256(rows * sh.num_qo_heads * 4);
+    L.total = L.lse_unique + align256((size_t)p->q_end * sh.num_qo_heads * 4);
+    return L;
+}
+
+size_t plan_workspace_bytes(const rp_plan *p)
+{
+    if (p == nullptr)
+        return 0;
+    return p->shared ? shared_layout(p).total : p->host.workspace_bytes();
+}
+
+// Validation of the state arrays of the merge entry points.
+int check_merge_shape(int64_t rows, int num_heads, int head_dim)
+{
+    if (rows < 0 || num_heads <= 0 || num_heads > 0xffff)
+        return fail(RP_EINVAL, "rows must be >= 0 and num_heads in [1, 65535]");
+    if (head_dim < 8 || head_dim > 512 || (head_dim & (head_dim - 1)) != 0)
+        return fail(RP_EINVAL, "head_dim must be a power of two in [8, 512]");
+    return RP_OK;
+}
+
+int launch_merge(const rp::StateMergeArgs &a, void *stream)
+{
+    const int st = rp::launch_state_merge(a, stream);
+    if (st != (int)hipSuccess)
+        return hip_fail((hipError_t)st, "state merge kernel launch");
+    return RP_OK;
+}
+
 // Paged K/V of one run (null: contiguous ragged K/V).
 struct PagedKV {
     const int32_t *block_table;
@@ -176,12 +229,14 @@ struct PagedKV {
 
 int run_plan(const rp_plan *p, const void *q, const void *k, const void *v, void *o, float *lse,
              float sm_scale, void *workspace, size_t workspace_bytes, void *stream,
-             const PagedKV *paged = nullptr)
+             const PagedKV *paged = nullptr, bool shared_level_call = false)
 {
     if (p == nullptr)
         return fail(RP_EINVAL, "plan must not be NULL");
     if (p->host_only)
         return fail(RP_EINVAL, "a host-only plan cannot be run");
+    if (p->shared && !shared_level_call)
+        return fail(RP_EINVAL, "a shared-prefix plan runs through rp_run_shared_prefix");
     if (!std::isfinite(sm_scale))
         return fail(RP_EINVAL, "sm_scale must be finite");
     const rp::HostPlan &h = p->host;
@@ -346,11 +401,21 @@ int rp_plan_get_info(const rp_plan *p, rp_plan_info *info)
     info->kv_chunk = h.shape.kv_chunk;
     info->flops = h.flops;
     info->bytes = h.bytes;
-    info->workspace_bytes = h.workspace_bytes();
+    if (p->shared) {
+        // both levels; algorithmic bytes add the shared K and V, read once
+        const rp::HostPlan &s = p->shared->host;
+        info->num_items += (int64_t)s.items.size();
+        info->num_partial_items += s.num_partial_items;
+        info->num_merge_items += (int64_t)s.merges.size();
+        info->total_kv += s.total_kv;
+        info->flops += s.flops;
+        info->bytes += 2.0 * 2.0 * (double)s.total_kv * h.shape.num_kv_heads * h.shape.head_dim;
+    }
+    info->workspace_bytes = plan_workspace_bytes(p);
     return RP_OK;
 }
 
-size_t rp_plan_workspace_bytes(const rp_plan *p) { return p ? p->host.workspace_bytes() : 0; }
+size_t rp_plan_workspace_bytes(const rp_plan *p) { return plan_workspace_bytes(p); }
 
 int64_t rp_plan_copy_items(const rp_plan *p, int32_t *dst, int64_t capacity)
 {
@@ -377,6 +442,170 @@ int rp_run_paged(const rp_plan *p, const void *q, const void *k_pages, const voi
 }
 
 void rp_plan_destroy(rp_plan *p) { free_plan(p); }
+
+int rp_plan_create_shared_prefix(const int32_t *q_indptr, const int32_t *kv_indptr, int batch,
+                                 int shared_kv_len, int num_qo_heads, int num_kv_heads,
+                                 int head_dim, int causal, const rp_plan_opts *opts, rp_plan **out)
+{
+    if (out == nullptr)
+        return fail(RP_EINVAL, "out must not be NULL");
+    *out = nullptr;
+    if (shared_kv_len < 0)
+        return fail(RP_EINVAL, "shared_kv_len must be >= 0");
+    if (batch < 0 || (batch > 0 && (q_indptr == nullptr || kv_indptr == nullptr)))
+        return fail(RP_EINVAL, "batch must be >= 0 and the offsets non-NULL");
+    if (causal) {
+        // Bottom-right causal over [prefix, own keys] shows the whole prefix to
+        // every row only if no request has more queries than own keys.
+        for (int b = 0; b < batch; ++b) {
+            const int64_t qo = (int64_t)q_indptr[b + 1] - q_indptr[b];
+            const int64_t kv = (int64_t)kv_indptr[b + 1] - kv_indptr[b];
+            if (qo > kv && shared_kv_len > 0)
+                return fail(RP_EINVAL, "causal shared-prefix attention needs qo_len <= kv_len "
+                                       "in every request (request " + std::to_string(b) + ")");
+        }
+    }
+    rp_plan *unique = nullptr;
+    int st = create_plan(q_indptr, kv_indptr, batch, num_qo_heads, num_kv_heads, head_dim, causal,
+                         opts, &unique);
+    if (st != RP_OK)
+        return st;
+    // the shared level: all query rows as one request over the prefix, no mask
+    const int64_t q0 = batch > 0 ? q_indptr[0] : 0, q1 = batch > 0 ? q_indptr[batch] : 0;
+    const int32_t sq[2] = {0, (int32_t)(q1 - q0)};
+    const int32_t skv[2] = {0, shared_kv_len};
+    rp_plan *shared = nullptr;
+    st = create_plan(sq, skv, 1, num_qo_heads, num_kv_heads, head_dim, 0, opts, &shared);
+    if (st != RP_OK) {
+        free_plan(unique);
+        return st;
+    }
+    unique->shared = shared;
+    unique->q_begin = q0;
+    unique->q_end = q1;
+    *out = unique;
+    return RP_OK;
+}
+
+int rp_run_shared_prefix(const rp_plan *p, const void *q, const void *k_shared,
+                         const void *v_shared, const void *k_unique, const void *v_unique, void *o,
+                         float *lse, float sm_scale, void *workspace, size_t workspace_bytes,
+                         void *stream)
+{
+    if (p == nullptr || p->shared == nullptr)
+        return fail(RP_EINVAL, "plan must come from rp_plan_create_shared_prefix");
+    if (p->host_only)
+        return fail(RP_EINVAL, "a host-only plan cannot be run");
+    if (p->q_end == p->q_begin)
+        return RP_OK;
+    if (q == nullptr || o == nullptr)
+        return fail(RP_EINVAL, "q and o must not be NULL");
+    const SharedLayout L = shared_layout(p);
+    if (workspace == nullptr || workspace_bytes < L.total)
+        return fail(RP_EINVAL, "workspace too small: need " + std::to_string(L.total) + " bytes");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(RP_EINVAL, "workspace must be 256-byte aligned");
+    const rp::PlanShape &sh = p->host.shape;
+    char *ws = static_cast<char *>(workspace);
+    const size_t row_elems = (size_t)sh.num_qo_heads * sh.head_dim;
+    const size_t row_bytes = row_elems * 2;  // bf16
+    const void *q_rows = static_cast<const char *>(q) + (size_t)p->q_begin * row_bytes;
+    void *o_shared = ws + L.o_shared;
+    float *lse_shared = reinterpret_cast<float *>(ws + L.lse_shared);
+    float *lse_unique = reinterpret_cast<float *>(ws + L.lse_unique);
+    // 1. every query row against the shared prefix (one request, no mask)
+    int st = run_plan(p->shared, q_rows, k_shared, v_shared, o_shared, lse_shared, sm_scale, ws,
+                      L.o_shared, stream, nullptr, true);
+    if (st != RP_OK)
+        return st;
+    // 2. each request against its own keys, into o
+    st = run_plan(p, q, k_unique, v_unique, o, lse_unique, sm_scale, ws, L.o_shared, stream,
+                  nullptr, true);
+    if (st != RP_OK)
+        return st;
+    // 3. o, lse = merge(shared state, own state), in place over o
+    rp::StateMergeArgs a{};
+    a.v0 = o_shared;
+    a.s0 = lse_shared;
+    a.v1 = static_cast<char *>(o) + (size_t)p->q_begin * row_bytes;
+    a.s1 = lse_unique + (size_t)p->q_begin * sh.num_qo_heads;
+    a.v_out = const_cast<void *>(a.v1);
+    a.s_out = lse ? lse + (size_t)p->q_begin * sh.num_qo_heads : nullptr;
+    a.v_row_stride = (int64_t)row_elems;
+    a.s_row_stride = sh.num_qo_heads;
+    a.rows = p->q_end - p->q_begin;
+    a.num_heads = sh.num_qo_heads;
+    a.head_dim = sh.head_dim;
+    a.num_states = 2;
+    return launch_merge(a, stream);
+}
+
+int rp_merge_state(const void *v_a, const float *s_a, const void *v_b, const float *s_b,
+                   void *v_out, float *s_out, int64_t rows, int num_heads, int head_dim,
+                   void *stream)
+{
+    int st = check_merge_shape(rows, num_heads, head_dim);
+    if (st != RP_OK)
+        return st;
+    if (rows == 0)
+        return RP_OK;
+    if (!v_a || !s_a || !v_b || !s_b || !v_out)
+        return fail(RP_EINVAL, "v_a, s_a, v_b, s_b and v_out must not be NULL");
+    if (!aligned16(v_a) || !aligned16(v_b) || !aligned16(v_out))
+        return fail(RP_EINVAL, "v_a, v_b and v_out must be 16-byte aligned");
+    rp::StateMergeArgs a{};
+    a.v0 = v_a;
+    a.v1 = v_b;
+    a.s0 = s_a;
+    a.s1 = s_b;
+    a.v_out = v_out;
+    a.s_out = s_out;
+    a.v_row_stride = (int64_t)num_heads * head_dim;
+    a.s_row_stride = num_heads;
+    a.rows = rows;
+    a.num_heads = num_heads;
+    a.head_dim = head_dim;
+    a.num_states = 2;
+    return launch_merge(a, stream);
+}
+
+int rp_merge_state_in_place(void *v, float *s, const void *v_other, const float *s_other,
+                            int64_t rows, int num_heads, int head_dim, void *stream)
+{
+    if (s == nullptr)
+        return fail(RP_EINVAL, "s must not be NULL");
+    return rp_merge_state(v, s, v_other, s_other, v, s, rows, num_heads, head_dim, stream);
+}
+
+int rp_merge_states(const void *v, const float *s, void *v_out, float *s_out, int64_t rows,
+                    int num_states, int num_heads, int head_dim, void *stream)
+{
+    int st = check_merge_shape(rows, num_heads, head_dim);
+    if (st != RP_OK)
+        return st;
+    if (num_states < 1)
+        return fail(RP_EINVAL, "num_states must be >= 1");
+    if (rows == 0)
+        return RP_OK;
+    if (!v || !s || !v_out)
+        return fail(RP_EINVAL, "v, s and v_out must not be NULL");
+    if (!aligned16(v) || !aligned16(v_out))
+        return fail(RP_EINVAL, "v and v_out must be 16-byte aligned");
+    rp::StateMergeArgs a{};
+    a.v0 = v;
+    a.s0 = s;
+    a.v_out = v_out;
+    a.s_out = s_out;
+    a.v_state_stride = (int64_t)num_heads * head_dim;
+    a.v_row_stride = (int64_t)num_states * num_heads * head_dim;
+    a.s_state_stride = num_heads;
+    a.s_row_stride = (int64_t)num_states * num_heads;
+    a.rows = rows;
+    a.num_heads = num_heads;
+    a.head_dim = head_dim;
+    a.num_states = num_states;
+    return launch_merge(a, stream);
+}
 
 int ragged_prefill_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
                         const int32_t *q_indptr, const int32_t *kv_indptr, int batch,
