@@ -11,7 +11,13 @@ design), the tile kernel and, when the plan splits KV, the merge kernel.
 Prints ONE JSON line.
 
 Default workload: 8 requests, qo_len = kv_len ~ U[128, 2048] (recorded lengths),
-32 qo / 8 kv heads, head_dim 128, causal, bf16 N(0,1) inputs.
+32 qo / 8 kv heads, head_dim 128, causal, bf16 N(0,1) inputs.  Without --warmup,
+the untimed warmup runs for at least 0.3 s (the GPU needs tens of ms of sustained
+load to reach its steady clock; 20 steps of this workload are 2 ms).
+
+roofline.bound is "mfma" when the workload's algorithmic flop/byte ratio is at
+or above the MI355X ridge (2.5 PF/s / 8 TB/s = 312.5 flop/B), else "hbm" (decode-
+like batches), with achieved algorithmic GB/s against 8 TB/s.
 
 Other modes:
   --paged P            the same batch with K/V scattered into a page pool of
@@ -52,7 +58,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "ragged causal prefill TFLOP/s & tok/s (bf16 GQA hd128) + % of MFMA peak"
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+WARMUP_SECONDS = 0.3             # default warmup: at least this much wall time of steps
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E (published)
+RIDGE_FLOP_PER_BYTE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)   # 312.5
 KERNEL_SRC = os.path.join(ROOT, "varlen_prefill_amd", "csrc", "rp_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{kernel}_{workload}.json")
 
@@ -66,7 +74,10 @@ def parse_args():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=None,
+                   help="untimed warmup steps (default: as many as take >= %.1f s, at least 20; "
+                        "the GPU needs tens of ms of sustained load to reach its steady clock)"
+                        % WARMUP_SECONDS)
     p.add_argument("--workload", default="hd128_gqa_causal")
     p.add_argument("--noncausal", action="store_true", help="run the workload without the causal mask")
     p.add_argument("--shared-prefix", type=int, default=0, metavar="P",
@@ -194,12 +205,30 @@ def load_traffic(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def _time_steps(step, warmup: int, steps: int, stream):
-    """Wall time and HIP-event time (on `stream`) of `steps` calls, ms/step."""
+def warm_up(step, warmup) -> int:
+    """Run `warmup` untimed steps, or (None) steps until WARMUP_SECONDS of wall
+    time have passed and at least 20 ran.  Returns the number run."""
     import torch
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    if warmup is not None:
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        return warmup
+    n = 0
+    t0 = time.perf_counter()
+    while n < 20 or time.perf_counter() - t0 < WARMUP_SECONDS:
+        for _ in range(10):
+            step()
+        n += 10
+        torch.cuda.synchronize()
+    return n
+
+
+def _time_steps(step, warmup, steps: int, stream):
+    """Wall time and HIP-event time (on `stream`) of `steps` calls, ms/step,
+    and the number of warmup steps run."""
+    import torch
+    warmup = warm_up(step, warmup)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -209,7 +238,7 @@ def _time_steps(step, warmup: int, steps: int, stream):
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    return wall, ev0.elapsed_time(ev1) / steps
+    return wall, ev0.elapsed_time(ev1) / steps, warmup
 
 
 def bench_shared_prefix(args, cfg, causal: bool) -> dict:
@@ -242,7 +271,7 @@ def bench_shared_prefix(args, cfg, causal: bool) -> dict:
 
     def step_sp():
         _lib.check(lib.rp_run_shared_prefix(*sp_args), "rp_run_shared_prefix")
-    wall, gpu = _time_steps(step_sp, args.warmup, args.steps, stream)
+    wall, gpu, n_warm = _time_steps(step_sp, args.warmup, args.steps, stream)
     # the flat run over the same keys: every request holds its own copy of the prefix
     kf, vf = [], []
     for r in range(b.batch):
@@ -260,14 +289,14 @@ def bench_shared_prefix(args, cfg, causal: bool) -> dict:
 
     def step_flat():
         _lib.check(lib.rp_run(*f_args), "rp_run")
-    fwall, fgpu = _time_steps(step_flat, args.warmup, args.steps, stream)
+    fwall, fgpu, _ = _time_steps(step_flat, args.warmup, args.steps, stream)
     flops = info["flops"]
     assert abs(flops - flat.info["flops"]) < 1e-6 * flops
     value = flops / (wall * 1e-3) / 1e12
     achieved = flops / (gpu * 1e-3) / 1e12
     return {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": wall, "higher_is_better": True, "scaling": "weak",
+        "warmup": n_warm, "ms_per_step": wall, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{cfg.name}_shared{p_len}" + ("" if causal else "_noncausal"),
                    "requests": cfg.batch, "num_qo_heads": hq, "num_kv_heads": hkv,
@@ -306,12 +335,12 @@ def bench_merge_states(args, cfg) -> dict:
 
     def step():
         _lib.check(lib.rp_merge_states(*a), "rp_merge_states")
-    wall, gpu = _time_steps(step, args.warmup, args.steps, stream)
+    wall, gpu, n_warm = _time_steps(step, args.warmup, args.steps, stream)
     nbytes = rows * h * ((k + 1) * (2 * d + 4))       # read k states, write one
     gbs = nbytes / (gpu * 1e-3) / 1e9
     return {
         "metric": "state merge GB/s", "value": nbytes / (wall * 1e-3) / 1e9, "unit": "GB/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall,
+        "n_gpus": 1, "steps": args.steps, "warmup": n_warm, "ms_per_step": wall,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"merge_states_k{k}_{cfg.name}", "rows": rows, "num_states": k,
@@ -412,9 +441,7 @@ def main():
         step = lib.rp_run_paged
         step_name = "rp_run_paged"
 
-    for _ in range(args.warmup):
-        _lib.check(step(*call_args), step_name)
-    torch.cuda.synchronize()
+    n_warm = warm_up(lambda: _lib.check(step(*call_args), step_name), args.warmup)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -435,13 +462,24 @@ def main():
     achieved = flops / (gpu_ms_per_step * 1e-3) / 1e12
     kernel = f"tile_kernel_hd{cfg.head_dim}"
     traffic = load_traffic(kernel, workload)
+    alg_gbs = alg_bytes / (gpu_ms_per_step * 1e-3) / 1e9
+    kernels = kernel if launches == 1 else f"{kernel} + merge_kernel"
+    if flops / alg_bytes >= RIDGE_FLOP_PER_BYTE:
+        roofline = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                    "traffic": traffic, "kernel": kernels, "alg_hbm_gbs": alg_gbs}
+    else:
+        # below the ridge (decode-like batches): the HBM bound applies
+        roofline = {"bound": "hbm", "achieved": alg_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": alg_gbs / HBM_PEAK_GBS, "traffic": traffic, "kernel": kernels,
+                    "alg_tflops": achieved}
     result = {
         "metric": METRIC,
         "value": value,
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": n_warm,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -467,16 +505,7 @@ def main():
         "gpu_ms_per_step": gpu_ms_per_step,
         "launches_per_step": launches,
         "plan_ms_median": float(np.median(plan_times) * 1e3),
-        "roofline": {
-            "bound": "mfma",
-            "achieved": achieved,
-            "peak": MFMA_BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-            "traffic": traffic,
-            "kernel": kernel if launches == 1 else f"{kernel} + merge_kernel",
-            "alg_hbm_gbs": alg_bytes / (gpu_ms_per_step * 1e-3) / 1e9,
-        },
+        "roofline": roofline,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -220,7 +220,7 @@ def test_graph_capture_replays():
     plan.close()
 
 
-@pytest.mark.parametrize("name", ["hd128_gqa_causal", "ragged64"])
+@pytest.mark.parametrize("name", ["hd128_gqa_causal", "ragged64", "decode64", "decode_few", "mixed"])
 def test_full_size_config_sampled(name):
     """Full-size workloads in the benchmark's launch configuration: every head
     of the first/last 40 tokens of each request and 3000 random rows are

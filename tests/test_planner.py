@@ -2,7 +2,8 @@
 
 * coverage: for every request, kv head and query token, the work items cover
   exactly the visible keys [0, limit of the tile's last row) once, in
-  canonical request-relative chunks;
+  canonical request-relative chunks (kv_chunk keys; at most 2048 for
+  decode-like requests of at most 32 query rows);
 * split tiles have one merge item whose slots hold chunks 0..n-1 in order;
 * the plan of a request does not depend on the rest of the batch;
 * items are ordered longest-first; algorithmic flops/bytes follow the counting
@@ -58,6 +59,8 @@ def _check_plan(qo_lens, kv_lens, hq, hkv, d, causal, kv_chunk=0, q_base=0, kv_b
             slots.add(it[F["slot"]])
     n_expected = 0
     for b, (qo, kv) in enumerate(zip(qo_lens, kv_lens)):
+        # decode-like requests (at most 32 query rows) use chunks of at most 2048 keys
+        cb = min(chunk, 2048) if qo * g <= 32 else chunk
         for t0 in range(0, qo, tt):
             n_tok = min(tt, qo - t0)
             lim_last = _limit(t0 + n_tok - 1, qo, kv, causal)
@@ -71,8 +74,8 @@ def _check_plan(qo_lens, kv_lens, hq, hkv, d, causal, kv_chunk=0, q_base=0, kv_b
                     assert all(r[2] >= 0 for r in ranges)
                     assert ranges[0][0] == 0 and ranges[-1][1] == lim_last
                     for c, (kb, ke, slot, ch) in enumerate(ranges):
-                        assert ch == c and kb == c * chunk
-                        assert ke == min((c + 1) * chunk, lim_last)
+                        assert ch == c and kb == c * cb
+                        assert ke == min((c + 1) * cb, lim_last)
                         assert slot == ranges[0][2] + c
     assert not seen, f"items outside every tile: {list(seen)[:3]}"
     # the rows each item names lie in its request

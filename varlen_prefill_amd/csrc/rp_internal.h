@@ -26,6 +26,11 @@ constexpr int kThreads = 256;       // threads per tile workgroup
 constexpr int kMergeThreads = 256;  // threads per merge workgroup
 constexpr int kDefaultKvChunk = 8192;
 constexpr int kChunkAlign = 64;     // kv_chunk must be a multiple of this
+// Requests whose query rows (qo_len x group) fill at most kDecodeRows rows of a
+// tile (decode-like) are cut into chunks of min(kv_chunk, kDecodeChunk) keys:
+// their work is a long key scan with few rows, which needs the parallelism.
+constexpr int kDecodeRows = 32;
+constexpr int kDecodeChunk = 2048;
 constexpr int kDefaultXcds = 8;     // MI355X: 8 XCDs, workgroups dispatched round-robin
 // Key blocks are computed with P split into a bf16 hi part and a bf16 lo
 // remainder when the tile's first row sees at most this many keys (and, at

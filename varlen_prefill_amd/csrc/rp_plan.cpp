@@ -9,10 +9,15 @@
 // Items are ordered longest-first (LPT), so the hardware's in-order workgroup
 // dispatch approximates greedy longest-processing-time scheduling.
 //
-// The chunk grid is a property of the request alone, which keeps per-request
-// results independent of the batch ("balanced tile worklist" with automatic
-// split-KV, page "flashinfer-ai/flashinfer", attention API, task-scheduled
-// attention).
+// Decode-like requests (at most kDecodeRows query rows: qo_len x group) use
+// chunks of min(kv_chunk, kDecodeChunk) keys: one tile per kv head would scan
+// all of their keys serially (the split-KV of decode at low concurrency, page
+// "vllm-rlt PR #112", results notes).
+//
+// The chunk grid is a property of the request alone (its own qo_len and the
+// batch-wide head shape), which keeps per-request results independent of the
+// batch ("balanced tile worklist" with automatic split-KV, page
+// "flashinfer-ai/flashinfer", attention API, task-scheduled attention).
 #include "rp_plan.h"
 
 #include <algorithm>
@@ -179,7 +184,8 @@ int build_plan(const int32_t *q_indptr, const int32_t *kv_indptr, const PlanShap
     plan.tile_tokens = kTileRows / group;
     const int bk = key_block(shape.head_dim);
     const bool causal = shape.causal != 0;
-    const int64_t C = shape.kv_chunk;
+    const int64_t C_prefill = shape.kv_chunk;
+    const int64_t C_decode = std::min<int64_t>(shape.kv_chunk, kDecodeChunk);
 
     if (shape.batch > 0) {
         plan.max_q_row = q_indptr[shape.batch];
@@ -196,6 +202,7 @@ int build_plan(const int32_t *q_indptr, const int32_t *kv_indptr, const PlanShap
             pairs_total += (double)limit_of(i, qo, kv, causal);
         if (qo == 0)
             continue;
+        const int64_t C = qo * group <= kDecodeRows ? C_decode : C_prefill;
         for (int64_t t0 = 0; t0 < qo; t0 += plan.tile_tokens) {
             const int64_t n_tok = std::min<int64_t>(plan.tile_tokens, qo - t0);
             const int64_t lim_first = limit_of(t0, qo, kv, causal);

@@ -1,4 +1,4 @@
-"""The five synthetic ragged-prefill workloads, with their request lengths recorded.
+"""The synthetic ragged-prefill workloads, with their request lengths recorded.
 
 The lengths were drawn once with ``numpy.random.default_rng(seed)`` by the
 recipe written next to each entry and are stored here verbatim: NumPy does not
@@ -74,6 +74,26 @@ _APPEND_QO = [344, 557, 738, 635, 768, 776, 765, 302, 993, 683, 950, 464, 534, 9
               305, 543, 778, 350, 925, 518, 430, 674, 944, 935, 926, 491, 270, 854, 800,
               848, 256]
 
+# recipe: rng = default_rng(6); kv = rng.integers(1024, 16385, 64); qo = 1 each
+_DECODE_KV = [7860, 9290, 8977, 6296, 15557, 6693, 11127, 6776, 7935, 16192, 3889, 10743,
+              7582, 11382, 12632, 6092, 11350, 11468, 7966, 2912, 10509, 1818, 14632, 14083,
+              14023, 1160, 15947, 16058, 10023, 13727, 12814, 13085, 3383, 1762, 5097, 4210,
+              9446, 14078, 12514, 7667, 9371, 10662, 12844, 2902, 12979, 3886, 9853, 8662,
+              14188, 12690, 3625, 9316, 1760, 2665, 8272, 14329, 4341, 3169, 15585, 7777,
+              2848, 10038, 6050, 5926]
+
+# recipe: rng = default_rng(7); kv = rng.integers(16384, 32769, 4); qo = 1 each
+_DECODE_FEW_KV = [31866, 26626, 27594, 31084]
+
+# recipe: rng = default_rng(8); p = rng.integers(512, 2049, 4) (prefill, qo = kv = p);
+#         d = rng.integers(1024, 8193, 60) (decode, qo = 1, kv = d), drawn after p
+_MIXED_PREFILL = [1617, 1014, 872, 2029]
+_MIXED_DECODE = [2285, 3308, 5630, 6677, 5610, 7260, 1370, 3827, 5136, 4163, 3810, 3696, 1311,
+                 1790, 4914, 4457, 7893, 2754, 7109, 2867, 2049, 2348, 3875, 2413, 7445, 6858,
+                 6791, 4056, 1241, 2858, 4218, 5260, 4249, 5356, 3738, 5661, 1220, 7557, 4866,
+                 2100, 6869, 3686, 7301, 3064, 7427, 1144, 4127, 2325, 4151, 3853, 8101, 3843,
+                 6453, 5445, 3805, 4266, 1578, 5377, 3867, 2623]
+
 
 CONFIGS: Dict[str, WorkloadConfig] = {
     "tiny": WorkloadConfig(
@@ -98,9 +118,24 @@ CONFIGS: Dict[str, WorkloadConfig] = {
         num_kv_heads=8, head_dim=128, causal=True, seed=5,
         description="32 requests kv~U[4096,16384], qo~U[256,1024], causal aligned to the end "
                     "of each KV, 64/8 heads, hd128"),
+    "decode64": WorkloadConfig(
+        name="decode64", qo_lens=[1] * 64, kv_lens=_DECODE_KV, num_qo_heads=32,
+        num_kv_heads=8, head_dim=128, causal=True, seed=6,
+        description="64 decode requests (qo=1), kv~U[1024,16384], 32/8 heads, hd128"),
+    "decode_few": WorkloadConfig(
+        name="decode_few", qo_lens=[1] * 4, kv_lens=_DECODE_FEW_KV, num_qo_heads=32,
+        num_kv_heads=8, head_dim=128, causal=True, seed=7,
+        description="4 decode requests (qo=1), kv~U[16384,32768], 32/8 heads, hd128 "
+                    "(low concurrency: needs split-KV)"),
+    "mixed": WorkloadConfig(
+        name="mixed", qo_lens=_MIXED_PREFILL + [1] * 60, kv_lens=_MIXED_PREFILL + _MIXED_DECODE,
+        num_qo_heads=32, num_kv_heads=8, head_dim=128, causal=True, seed=8,
+        description="4 prefill requests qo=kv~U[512,2048] and 60 decode requests (qo=1, "
+                    "kv~U[1024,8192]) in one batch, 32/8 heads, hd128"),
 }
 
-CONFIG_ORDER: List[str] = ["tiny", "hd128_gqa_causal", "hd256_gqa", "ragged64", "append_prefix"]
+CONFIG_ORDER: List[str] = ["tiny", "hd128_gqa_causal", "hd256_gqa", "ragged64", "append_prefix",
+                           "decode64", "decode_few", "mixed"]
 
 
 def get_config(name: str) -> WorkloadConfig:
