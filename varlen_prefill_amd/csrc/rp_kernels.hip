@@ -347,6 +347,14 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
             lane_offsets(lane, i, grow_[i], kcol[i], vcol[i]);
     }
     const int kv_stride_i = a.num_kv_heads * HD;
+    unsigned koff0[T::NLOAD], voff0[T::NLOAD];
+#pragma unroll
+    for (int i = 0; i < (HD == 128 ? T::NLOAD : 0); ++i) {
+        int gr, kc, vc;
+        lane_offsets(lane, i, gr, kc, vc);
+        koff0[i] = (unsigned)(gr * kv_stride_i + kc) * 2u;
+        voff0[i] = (unsigned)(gr * kv_stride_i + vc) * 2u;
+    }
     const unsigned lds_base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
     // Paged K/V: a wave's loads of one block move WAVE_ROWS aligned
     // consecutive keys (clamped to the request's last key), so with pages of
@@ -373,6 +381,19 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
         const __bf16 *kb_ptr = kbase + blk;
         const __bf16 *vb_ptr = vbase + blk;
         const int last = it.kv_len - 1 - kb * T::BK;
+        if (!PAGED && HD == 128 && last >= T::BK - 1) {
+            // whole block inside the request: no clamping, constant lane offsets
+#pragma unroll
+            for (int i = 0; i < T::NLOAD; ++i) {
+                const unsigned dk = lds_base + (unsigned)(buf * T::STAGE_BYTES + (T::NLOAD * wu + i) * 1024);
+                asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                             :: "s"(dk), "v"(koff0[i]), "s"(kb_ptr) : "memory", "m0");
+                asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                             :: "s"(dk + (unsigned)T::TILE_BYTES), "v"(voff0[i]), "s"(vb_ptr)
+                             : "memory", "m0");
+            }
+            return;
+        }
         int ln = lane;
         if constexpr (!KEEP_OFFSETS) {
             ln = __lane_id();
@@ -415,12 +436,14 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
     };
 
     // The first blocks' K/V loads go out before the Q loads so that the
-    // latencies overlap.  Block kb lives in stage (kb - kb_begin) % STAGES.
+    // latencies overlap.  Block kb lives in stage kb % STAGES (absolute block
+    // parity, so that the unrolled loop below knows every stage at compile
+    // time and LDS addresses become per-lane constants plus an immediate).
     const int kb_pre = min(kb_begin + T::STAGES - 1, kb_end);
     for (int kb = kb_begin; kb < kb_pre; ++kb) {
         if (PAGED)
             page_id(kb);
-        issue_loads(kb, kb - kb_begin);
+        issue_loads(kb, HD == 128 ? kb % T::STAGES : kb - kb_begin);
     }
     if (PAGED && kb_pre < kb_end)
         page_id(kb_pre);
@@ -464,22 +487,51 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
     auto run = [&](auto mask_tag, auto hilo_tag, int kb_from, int kb_to) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
         constexpr bool HILO = decltype(hilo_tag)::value;
-        for (int kb = kb_from; kb < kb_to; ++kb) {
-            const int buf = (kb - kb_begin) % T::STAGES;
-            if (kb + T::STAGES - 1 < kb_end) {
-                issue_loads(kb + T::STAGES - 1, (kb + T::STAGES - 1 - kb_begin) % T::STAGES);
-                // the page ids of the block loaded next iteration
-                if (PAGED && kb + T::STAGES < kb_end)
-                    page_id(kb + T::STAGES);
+        static_assert(T::STAGES == 2, "the loops assume two stages");
+        if constexpr (HD != 128) {
+            // head_dim 256: stage (kb - kb_begin) % STAGES, one block per iteration
+            for (int kb = kb_from; kb < kb_to; ++kb) {
+                const int buf = (kb - kb_begin) % T::STAGES;
+                if (kb + T::STAGES - 1 < kb_end) {
+                    issue_loads(kb + T::STAGES - 1, (kb + T::STAGES - 1 - kb_begin) % T::STAGES);
+                    if (PAGED && kb + T::STAGES < kb_end)
+                        page_id(kb + T::STAGES);
+                }
+                const char *Ks = smem + buf * T::STAGE_BYTES;
+                const char *Vs = Ks + T::TILE_BYTES;
+                const int thr = lim_row - kb * T::BK - 4 * h;
+                block_step<HD, POS_SCALE, MASK, HILO>(st, Ks, Vs, c, thr, qc, h, grp, s16);
+                wait_loads(min(kb_end, kb + T::STAGES) - (kb + 2));
+                __syncthreads();
             }
-            const char *Ks = smem + buf * T::STAGE_BYTES;
+            return;
+        }
+        auto step = [&](int kb, auto buf_tag) __attribute__((always_inline)) {
+            constexpr int BUF = decltype(buf_tag)::value;
+            if (kb + 1 < kb_end) {
+                issue_loads(kb + 1, BUF ^ 1);
+                // the page ids of the block loaded next iteration
+                if (PAGED && kb + 2 < kb_end)
+                    page_id(kb + 2);
+            }
+            const char *Ks = smem + BUF * T::STAGE_BYTES;
             const char *Vs = Ks + T::TILE_BYTES;
             const int thr = lim_row - kb * T::BK - 4 * h;
             block_step<HD, POS_SCALE, MASK, HILO>(st, Ks, Vs, c, thr, qc, h, grp, s16);
-            // block kb + 1 must have landed; later ones may stay in flight
-            wait_loads(min(kb_end, kb + T::STAGES) - (kb + 2));
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // block kb + 1 has landed
             __syncthreads();
+        };
+        int kb = kb_from;
+        if (kb < kb_to && (kb & 1)) {
+            step(kb, std::integral_constant<int, 1>{});
+            ++kb;
         }
+        for (; kb + 1 < kb_to; kb += 2) {
+            step(kb, std::integral_constant<int, 0>{});
+            step(kb + 1, std::integral_constant<int, 1>{});
+        }
+        if (kb < kb_to)
+            step(kb, std::integral_constant<int, 0>{});
     };
     if constexpr (HD == 128) {
         if (hilo_all) {
