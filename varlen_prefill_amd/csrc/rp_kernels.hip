@@ -555,10 +555,23 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
     const float lt = pair_sum(st.l);
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
     const float lse2 = lt > 0.0f ? st.m + log2f(lt) : -INFINITY;
-    if (!row_valid)
-        return;
+    // The outputs go out through LDS (the K/V stages are free after the last
+    // block barrier; each wave uses its own region): the wave writes its
+    // O^T fragments as rows, 16-byte chunk c of row r at position
+    // c ^ (r mod chunks-per-row), reads back whole 16-byte row chunks, and
+    // stores full row segments, so that consecutive lanes write consecutive
+    // bytes (the g heads of a token are adjacent rows of O).
+    const float inv_g = 1.0f / (float)g;
+    auto row_out = [&](int rr, size_t &orow) __attribute__((always_inline)) {
+        const int R = w * 32 + rr;
+        const int tk = (int)(((float)R + 0.5f) * inv_g);
+        orow = (size_t)(it.q_tok0 + tk) * a.num_qo_heads + it.kv_head * g + (R - tk * g);
+        return tk < it.n_tok;
+    };
     if (it.slot < 0) {
-        __bf16 *op = static_cast<__bf16 *>(a.o) + q_row * HD + 4 * h;
+        constexpr int CPR = T::CPR;          // 16-byte chunks per bf16 row
+        constexpr int RPI = 64 / CPR;        // rows per read instruction
+        char *wl = smem + w * (32 * T::RB);
 #pragma unroll
         for (int db = 0; db < T::DB; ++db)
 #pragma unroll
@@ -567,24 +580,54 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     ov[e] = (__bf16)(st.acc[db][4 * jj + e] * inv);
-                *reinterpret_cast<bf16x4 *>(op + 32 * db + 8 * jj) = ov;
+                const int cc = 4 * db + jj;
+                *reinterpret_cast<bf16x4 *>(wl + qc * T::RB + 16 * (cc ^ (qc & (CPR - 1))) + 8 * h) = ov;
             }
-        if (h == 0 && a.lse != nullptr)
+#pragma unroll
+        for (int i = 0; i < 32 / RPI; ++i) {
+            const int rr = RPI * i + lane / CPR;
+            const int cc = lane % CPR;
+            const bf16x8 x = *reinterpret_cast<const bf16x8 *>(wl + rr * T::RB + 16 * (cc ^ (rr & (CPR - 1))));
+            size_t orow;
+            if (row_out(rr, orow))
+                *reinterpret_cast<bf16x8 *>(static_cast<__bf16 *>(a.o) + orow * HD + 8 * cc) = x;
+        }
+        if (row_valid && h == 0 && a.lse != nullptr)
             a.lse[q_row] = lse2 == -INFINITY ? -INFINITY : lse2 * kLn2;
     } else {
-        float *pp = a.part_o + ((size_t)it.slot * kTileRows + r) * HD + 4 * h;
+        // fp32 partial state of the tile's rows, in two passes over d
+        constexpr int DBP = T::DB / 2;       // d blocks per pass
+        constexpr int CPRF = DBP * 8;        // 16-byte chunks per row and pass
+        constexpr int RPIF = 64 / CPRF;
+        char *wl = smem + w * (32 * CPRF * 16);
+        float *pbase = a.part_o + (size_t)it.slot * kTileRows * HD;
 #pragma unroll
-        for (int db = 0; db < T::DB; ++db)
+        for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                float4 ov;
-                ov.x = st.acc[db][4 * jj + 0] * inv;
-                ov.y = st.acc[db][4 * jj + 1] * inv;
-                ov.z = st.acc[db][4 * jj + 2] * inv;
-                ov.w = st.acc[db][4 * jj + 3] * inv;
-                *reinterpret_cast<float4 *>(pp + 32 * db + 8 * jj) = ov;
+            for (int dbl = 0; dbl < DBP; ++dbl)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int db = pass * DBP + dbl;
+                    float4 ov;
+                    ov.x = st.acc[db][4 * jj + 0] * inv;
+                    ov.y = st.acc[db][4 * jj + 1] * inv;
+                    ov.z = st.acc[db][4 * jj + 2] * inv;
+                    ov.w = st.acc[db][4 * jj + 3] * inv;
+                    const int cc = 8 * dbl + 2 * jj + h;
+                    *reinterpret_cast<float4 *>(wl + qc * (CPRF * 16) + 16 * (cc ^ (qc & (CPRF - 1)))) = ov;
+                }
+#pragma unroll
+            for (int i = 0; i < 32 / RPIF; ++i) {
+                const int rr = RPIF * i + lane / CPRF;
+                const int cc = lane % CPRF;
+                const float4 x = *reinterpret_cast<const float4 *>(
+                    wl + rr * (CPRF * 16) + 16 * (cc ^ (rr & (CPRF - 1))));
+                size_t orow;
+                if (row_out(rr, orow))
+                    *reinterpret_cast<float4 *>(pbase + (size_t)(w * 32 + rr) * HD + pass * DBP * 32 + 4 * cc) = x;
             }
-        if (h == 0)
+        }
+        if (row_valid && h == 0)
             a.part_lse[(size_t)it.slot * kTileRows + r] = lse2;
     }
 }
