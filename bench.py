@@ -20,6 +20,8 @@ or above the MI355X ridge (2.5 PF/s / 8 TB/s = 312.5 flop/B), else "hbm" (decode
 like batches), with achieved algorithmic GB/s against 8 TB/s.
 
 Other modes:
+  --kv-fp8             K/V stored as FP8 E4M3 codes (per-tensor scales); the
+                       algorithmic bytes count K/V at one byte per element.
   --paged P            the same batch with K/V scattered into a page pool of
                        P-key pages in random order; a step is one rp_run_paged
                        call on a plan built once before the timed region.
@@ -86,6 +88,9 @@ def parse_args():
                         "flat run over the same keys")
     p.add_argument("--merge-states", type=int, default=0, metavar="K",
                    help="time rp_merge_states over K states per (token, qo head) of the workload")
+    p.add_argument("--kv-fp8", action="store_true",
+                   help="K/V as FP8 E4M3 codes with per-tensor scales max|x| / 448 "
+                        "(rp_run_fp8kv / rp_run_paged_fp8kv on a prebuilt plan)")
     p.add_argument("--paged", type=int, default=0, metavar="PAGE_SIZE",
                    help="keep K/V in a paged cache of this page size (rp_run_paged on a prebuilt plan)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -390,7 +395,8 @@ def main():
                else bench_merge_states(args, cfg))
         print(json.dumps(res))
         return
-    workload = cfg.name + ("" if causal else "_noncausal") + (f"_paged{args.paged}" if args.paged else "")
+    workload = (cfg.name + ("" if causal else "_noncausal") + ("_fp8kv" if args.kv_fp8 else "")
+                + (f"_paged{args.paged}" if args.paged else ""))
     batch = make_config_batch(cfg)
     sm_scale = float(np.float32(1.0 / math.sqrt(cfg.head_dim)))
     dev = torch.device("cuda:0")
@@ -425,7 +431,36 @@ def main():
                  ctypes.c_void_p(stream.cuda_stream))
     step = lib.ragged_prefill_bf16
     step_name = "ragged_prefill_bf16"
-    if args.paged:
+    if args.kv_fp8:
+        from workloads import make_fp8_kv, make_paged
+        ks = float(batch.k.float().abs().max()) / 448.0
+        vs = float(batch.v.float().abs().max()) / 448.0
+        k8, v8 = make_fp8_kv(batch, ks, vs)
+        fplan = vp.Plan(batch.q_indptr, batch.kv_indptr, cfg.num_qo_heads, cfg.num_kv_heads,
+                        cfg.head_dim, causal)
+        ws = torch.empty(max(fplan.workspace_bytes, 1), dtype=torch.uint8, device=dev)
+        if args.paged:
+            pk = make_paged(batch, args.paged, seed=cfg.seed, k=k8, v=v8)
+            kp, vpg = pk.k_pages.to(dev), pk.v_pages.to(dev)
+            table = torch.from_numpy(pk.block_table).to(dev)
+            call_args = (fplan.handle, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(kp.data_ptr()),
+                         ctypes.c_void_p(vpg.data_ptr()), ctypes.c_void_p(table.data_ptr()),
+                         int(table.shape[1]), args.paged, ctypes.c_float(ks), ctypes.c_float(vs),
+                         ctypes.c_void_p(o.data_ptr()), ctypes.c_void_p(lse.data_ptr()),
+                         ctypes.c_float(sm_scale), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                         ctypes.c_void_p(stream.cuda_stream))
+            step, step_name = lib.rp_run_paged_fp8kv, "rp_run_paged_fp8kv"
+        else:
+            k8d, v8d = k8.to(dev), v8.to(dev)
+            call_args = (fplan.handle, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k8d.data_ptr()),
+                         ctypes.c_void_p(v8d.data_ptr()), ctypes.c_float(ks), ctypes.c_float(vs),
+                         ctypes.c_void_p(o.data_ptr()), ctypes.c_void_p(lse.data_ptr()),
+                         ctypes.c_float(sm_scale), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                         ctypes.c_void_p(stream.cuda_stream))
+            step, step_name = lib.rp_run_fp8kv, "rp_run_fp8kv"
+        # K and V at one byte per element
+        alg_bytes -= 2.0 * cfg.num_kv_heads * cfg.head_dim * cfg.total_kv
+    elif args.paged:
         from workloads import make_paged
         pk = make_paged(batch, args.paged, seed=cfg.seed)
         kp, vpg = pk.k_pages.to(dev), pk.v_pages.to(dev)
@@ -497,6 +532,7 @@ def main():
             "total_kv": cfg.total_kv,
             "seed": cfg.seed,
             "kv_layout": f"paged, page_size {args.paged}" if args.paged else "ragged",
+            "kv_dtype": "fp8_e4m3 (per-tensor scales)" if args.kv_fp8 else "bf16",
         },
         "tokens_per_s": cfg.total_q / (ms_per_step * 1e-3),
         "mfma_peak_frac": value / MFMA_BF16_PEAK_TFLOPS,

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define RP_ABI_VERSION 3
+#define RP_ABI_VERSION 4
 
 /* Status codes. */
 enum rp_status {
@@ -190,6 +190,26 @@ int rp_run_paged(const rp_plan *plan, const void *q, const void *k_pages, const 
                  const int32_t *block_table, int max_blocks_per_seq, int page_size, void *o,
                  float *lse, float sm_scale, void *workspace, size_t workspace_bytes,
                  void *stream);
+
+/* FP8 K/V (the FP8 KV cache of page "flashinfer-ai/flashinfer", benchmarks
+ * README, attention flags --q_dtype / --kv_dtype fp8_e4m3): k and v hold OCP
+ * FP8 E4M3 codes (one byte per element, same NHD layout and offsets as
+ * rp_run, 16-byte aligned), dequantised as code x k_scale and code x
+ * v_scale (per-tensor scales, finite).  Q, O and LSE are as for rp_run (bf16
+ * Q and O).  The result is the attention over the dequantised K and V; the
+ * E4M3 codes convert to bf16 exactly, k_scale is folded into the softmax
+ * scale and v_scale into the output normalisation.  head_dim must be 128
+ * (RP_EUNSUPPORTED otherwise).  Codes 0x7f / 0xff (NaN) give NaN. */
+int rp_run_fp8kv(const rp_plan *plan, const void *q, const void *k_fp8, const void *v_fp8,
+                 float k_scale, float v_scale, void *o, float *lse, float sm_scale,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* rp_run_paged with FP8 (E4M3) page pools [num_pages][page_size]
+ * [num_kv_heads][head_dim] bytes; scales and limits as for rp_run_fp8kv. */
+int rp_run_paged_fp8kv(const rp_plan *plan, const void *q, const void *k_pages, const void *v_pages,
+                       const int32_t *block_table, int max_blocks_per_seq, int page_size,
+                       float k_scale, float v_scale, void *o, float *lse, float sm_scale,
+                       void *workspace, size_t workspace_bytes, void *stream);
 
 /* Destroys a plan of either kind (a shared-prefix plan frees both levels). */
 void rp_plan_destroy(rp_plan *plan);

@@ -166,6 +166,62 @@ def paged_kv_gather(k_pages, v_pages, block_table, kv_lens: Sequence[int], page_
     return k, v, indptr
 
 
+def e4m3_to_f64(codes) -> np.ndarray:
+    """Values of OCP FP8 E4M3 codes (uint8), from the format's definition:
+    1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits; exponent 0 is
+    subnormal (m x 2^-9); exponent 15 with mantissa 7 is NaN (no infinities),
+    largest finite 448.  The FP8 K/V dtype of page "flashinfer-ai/flashinfer",
+    benchmarks README, attention flags (--kv_dtype fp8_e4m3)."""
+    b = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where((b >> 7) != 0, -1.0, 1.0)
+    e = (b >> 3) & 15
+    m = b & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+def fp8_kv_attention(q, k_fp8, v_fp8, k_scale: float, v_scale: float, q_indptr, kv_indptr,
+                     num_qo_heads: int, num_kv_heads: int, causal: bool, sm_scale: float,
+                     fill: float = np.nan) -> Tuple[np.ndarray, np.ndarray]:
+    """Attention over FP8 K/V (fp64, numpy): K = code x k_scale and
+    V = code x v_scale are dequantised exactly, then for every request and
+    qo head S = sm_scale Q K^T, the bottom-right causal mask, P = softmax(S),
+    O = P V and LSE = log sum exp(S) over the visible keys (rows that see no
+    key: O = 0, LSE = -inf).  Written independently of the C oracle."""
+    qb = _bits(q)
+    qf = (qb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    kf = e4m3_to_f64(np.asarray(k_fp8)) * float(k_scale)
+    vf = e4m3_to_f64(np.asarray(v_fp8)) * float(v_scale)
+    rows, hq, d = qf.shape
+    g = num_qo_heads // num_kv_heads
+    o = np.full((rows, hq, d), fill, dtype=np.float64)
+    lse = np.full((rows, hq), fill, dtype=np.float64)
+    qi = np.asarray(q_indptr, dtype=np.int64)
+    ki = np.asarray(kv_indptr, dtype=np.int64)
+    for b in range(len(qi) - 1):
+        qo, kv = qi[b + 1] - qi[b], ki[b + 1] - ki[b]
+        if qo == 0:
+            continue
+        i = np.arange(qo)[:, None]
+        j = np.arange(kv)[None, :]
+        visible = (j <= i + kv - qo) if causal else np.ones((qo, kv), dtype=bool)
+        for h in range(hq):
+            Q = qf[qi[b]:qi[b + 1], h, :]
+            K = kf[ki[b]:ki[b + 1], h // g, :]
+            V = vf[ki[b]:ki[b + 1], h // g, :]
+            S = np.where(visible, sm_scale * (Q @ K.T), -np.inf)
+            m = S.max(axis=1, initial=-np.inf)
+            none = np.isneginf(m)
+            msafe = np.where(none, 0.0, m)
+            P = np.exp(S - msafe[:, None])
+            lsum = P.sum(axis=1)
+            out = (P @ V) / np.where(none, 1.0, lsum)[:, None]
+            o[qi[b]:qi[b + 1], h, :] = np.where(none[:, None], 0.0, out)
+            lse[qi[b]:qi[b + 1], h] = np.where(none, -np.inf, msafe + np.log(np.where(none, 1.0, lsum)))
+    return o, lse
+
+
 def ragged_attention_rows(q, k, v, q_indptr, kv_indptr, num_qo_heads: int, num_kv_heads: int,
                           causal: bool, sm_scale: float, tokens, heads, lib=None
                           ) -> Tuple[np.ndarray, np.ndarray]:

@@ -11,6 +11,7 @@ Entry points:
   ragged_prefill(q, k, v, q_indptr, kv_indptr, ...)  one-shot (plans are cached)
   Plan(q_indptr, kv_indptr, ...).run(q, k, v, ...)   plan once, run many
   Plan(...).run_paged(q, k_pages, v_pages, block_table, ...)   K/V in a paged cache
+  Plan(...).run_fp8kv / run_paged_fp8kv(...)          FP8 (E4M3) K/V with per-tensor scales
   SharedPrefixPlan(q_indptr, kv_indptr, shared_kv_len, ...).run(q, k_shared, v_shared,
                    k_unique, v_unique, ...)            shared-prefix (cascade) attention
   merge_state / merge_state_in_place / merge_states    merging attention states (v, lse)
@@ -191,6 +192,78 @@ class Plan:
         _lib.check(st, "rp_run")
         return out, lse
 
+    def _outputs(self, q, out, lse, return_lse, workspace):
+        import torch
+        rows_q = int(self.q_indptr[-1])
+        if out is None:
+            out = torch.empty_like(q)
+        else:
+            _check_tensor(out, "out", rows_q, self.num_qo_heads, self.head_dim)
+        if lse is None and return_lse:
+            lse = torch.empty((q.shape[0], self.num_qo_heads), dtype=torch.float32, device=q.device)
+        if lse is not None:
+            _check_lse(lse, rows_q, self.num_qo_heads, q.device)
+        need = self.workspace_bytes
+        if workspace is None and need > 0:
+            if self._workspace is None or self._workspace.numel() < need:
+                self._workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            workspace = self._workspace
+        ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        return out, lse, ws_ptr, ws_bytes
+
+    def run_fp8kv(self, q, k_fp8, v_fp8, k_scale: float, v_scale: float, out=None, lse=None,
+                  sm_scale: Optional[float] = None, return_lse: bool = True, workspace=None,
+                  stream=None):
+        """Run with FP8 (OCP E4M3) K/V: k_fp8, v_fp8 uint8 (or float8_e4m3fn)
+        [rows_kv, num_kv_heads, head_dim] on the GPU, dequantised as code x
+        k_scale / code x v_scale (head_dim 128)."""
+        rows_q = int(self.q_indptr[-1])
+        rows_kv = int(self.kv_indptr[-1])
+        _check_tensor(q, "q", rows_q, self.num_qo_heads, self.head_dim)
+        for name, t in (("k_fp8", k_fp8), ("v_fp8", v_fp8)):
+            _check_fp8(t, name, rows_kv, self.num_kv_heads, self.head_dim, 3)
+        out, lse, ws_ptr, ws_bytes = self._outputs(q, out, lse, return_lse, workspace)
+        scale = _default_scale(self.head_dim) if sm_scale is None else float(sm_scale)
+        st = self._lib.rp_run_fp8kv(self.handle, ctypes.c_void_p(q.data_ptr()),
+                                    ctypes.c_void_p(k_fp8.data_ptr()), ctypes.c_void_p(v_fp8.data_ptr()),
+                                    ctypes.c_float(k_scale), ctypes.c_float(v_scale),
+                                    ctypes.c_void_p(out.data_ptr()),
+                                    ctypes.c_void_p(lse.data_ptr()) if lse is not None else None,
+                                    ctypes.c_float(scale), ws_ptr, ws_bytes, _stream_handle(stream))
+        _lib.check(st, "rp_run_fp8kv")
+        return out, lse
+
+    def run_paged_fp8kv(self, q, k_pages, v_pages, block_table, k_scale: float, v_scale: float,
+                        out=None, lse=None, sm_scale: Optional[float] = None,
+                        return_lse: bool = True, workspace=None, stream=None):
+        """run_paged with FP8 (OCP E4M3) page pools [num_pages, page_size,
+        num_kv_heads, head_dim] (uint8 or float8_e4m3fn), head_dim 128."""
+        import torch
+        rows_q = int(self.q_indptr[-1])
+        _check_tensor(q, "q", rows_q, self.num_qo_heads, self.head_dim)
+        for name, t in (("k_pages", k_pages), ("v_pages", v_pages)):
+            _check_fp8(t, name, None, self.num_kv_heads, self.head_dim, 4)
+        if k_pages.shape != v_pages.shape:
+            raise ValueError("k_pages and v_pages must have the same shape")
+        if (not isinstance(block_table, torch.Tensor) or block_table.device.type != "cuda"
+                or block_table.dtype != torch.int32 or block_table.dim() != 2
+                or block_table.shape[0] != self.batch or not block_table.is_contiguous()):
+            raise ValueError(f"block_table must be a contiguous int32 [{self.batch}, max_blocks] GPU tensor")
+        out, lse, ws_ptr, ws_bytes = self._outputs(q, out, lse, return_lse, workspace)
+        scale = _default_scale(self.head_dim) if sm_scale is None else float(sm_scale)
+        st = self._lib.rp_run_paged_fp8kv(self.handle, ctypes.c_void_p(q.data_ptr()),
+                                          ctypes.c_void_p(k_pages.data_ptr()),
+                                          ctypes.c_void_p(v_pages.data_ptr()),
+                                          ctypes.c_void_p(block_table.data_ptr()),
+                                          int(block_table.shape[1]), int(k_pages.shape[1]),
+                                          ctypes.c_float(k_scale), ctypes.c_float(v_scale),
+                                          ctypes.c_void_p(out.data_ptr()),
+                                          ctypes.c_void_p(lse.data_ptr()) if lse is not None else None,
+                                          ctypes.c_float(scale), ws_ptr, ws_bytes, _stream_handle(stream))
+        _lib.check(st, "rp_run_paged_fp8kv")
+        return out, lse
+
     def run_paged(self, q, k_pages, v_pages, block_table, out=None, lse=None,
                   sm_scale: Optional[float] = None, return_lse: bool = True, workspace=None,
                   stream=None):
@@ -328,6 +401,18 @@ class SharedPrefixPlan(Plan):
 
     def run_paged(self, *args, **kwargs):
         raise RaggedPrefillError(-1, "a shared-prefix plan runs through run()")
+
+
+def _check_fp8(t, name: str, rows_needed, heads: int, head_dim: int, ndim: int) -> None:
+    import torch
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a GPU tensor")
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise TypeError(f"{name} must hold FP8 E4M3 codes (uint8 or float8_e4m3fn)")
+    if t.dim() != ndim or t.shape[-2] != heads or t.shape[-1] != head_dim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous [..., {heads}, {head_dim}] tensor of rank {ndim}")
+    if rows_needed is not None and t.shape[0] < rows_needed:
+        raise ValueError(f"{name} has {t.shape[0]} rows but the offsets need {rows_needed}")
 
 
 def _check_lse(t, rows: int, heads: int, device, name: str = "lse") -> None:

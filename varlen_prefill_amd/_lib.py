@@ -40,6 +40,8 @@ EXPORTS = [
     "rp_plan_copy_items",
     "rp_run",
     "rp_run_paged",
+    "rp_run_fp8kv",
+    "rp_run_paged_fp8kv",
     "rp_plan_destroy",
     "rp_merge_state",
     "rp_merge_state_in_place",
@@ -110,6 +112,11 @@ def load():
         lib.rp_run.restype = I
         lib.rp_run_paged.argtypes = [P, P, P, P, P, I, I, P, P, ctypes.c_float, P, ctypes.c_size_t, P]
         lib.rp_run_paged.restype = I
+        F = ctypes.c_float
+        lib.rp_run_fp8kv.argtypes = [P, P, P, P, F, F, P, P, F, P, ctypes.c_size_t, P]
+        lib.rp_run_fp8kv.restype = I
+        lib.rp_run_paged_fp8kv.argtypes = [P, P, P, P, P, I, I, F, F, P, P, F, P, ctypes.c_size_t, P]
+        lib.rp_run_paged_fp8kv.restype = I
         lib.rp_plan_destroy.argtypes = [P]
         lib.rp_plan_destroy.restype = None
         I64 = ctypes.c_int64

@@ -227,9 +227,16 @@ struct PagedKV {
     int page_size;
 };
 
+// FP8 (e4m3) K/V of one run (null: bf16 K/V): dequantised value = code x scale.
+struct Fp8KV {
+    float k_scale;
+    float v_scale;
+};
+
 int run_plan(const rp_plan *p, const void *q, const void *k, const void *v, void *o, float *lse,
              float sm_scale, void *workspace, size_t workspace_bytes, void *stream,
-             const PagedKV *paged = nullptr, bool shared_level_call = false)
+             const PagedKV *paged = nullptr, bool shared_level_call = false,
+             const Fp8KV *fp8 = nullptr)
 {
     if (p == nullptr)
         return fail(RP_EINVAL, "plan must not be NULL");
@@ -240,6 +247,12 @@ int run_plan(const rp_plan *p, const void *q, const void *k, const void *v, void
     if (!std::isfinite(sm_scale))
         return fail(RP_EINVAL, "sm_scale must be finite");
     const rp::HostPlan &h = p->host;
+    if (fp8) {
+        if (!std::isfinite(fp8->k_scale) || !std::isfinite(fp8->v_scale))
+            return fail(RP_EINVAL, "k_scale and v_scale must be finite");
+        if (h.shape.head_dim != 128)
+            return fail(RP_EUNSUPPORTED, "FP8 K/V is implemented for head_dim 128 only");
+    }
     if (h.items.empty())
         return RP_OK;  // empty batch / no query rows: nothing to launch
     if (q == nullptr || o == nullptr)
@@ -301,7 +314,8 @@ int run_plan(const rp_plan *p, const void *q, const void *k, const void *v, void
     ta.num_kv_heads = h.shape.num_kv_heads;
     ta.group = h.shape.num_qo_heads / h.shape.num_kv_heads;
     ta.causal = h.shape.causal;
-    ta.scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
+    ta.scale_log2 = (float)((double)sm_scale * (fp8 ? (double)fp8->k_scale : 1.0) * 1.4426950408889634);
+    ta.v_scale = fp8 ? fp8->v_scale : 1.0f;
     if (paged) {
         ta.block_table = paged->block_table;
         ta.max_blocks = paged->max_blocks;
@@ -309,7 +323,8 @@ int run_plan(const rp_plan *p, const void *q, const void *k, const void *v, void
     }
     logf(3, "launch tile kernel: D=%d items=%zu merges=%zu scale_log2=%g", h.shape.head_dim,
          h.items.size(), h.merges.size(), (double)ta.scale_log2);
-    int st = rp::launch_tile_kernel(h.shape.head_dim, paged != nullptr, ta, (int64_t)h.items.size(), stream);
+    int st = rp::launch_tile_kernel(h.shape.head_dim, paged != nullptr, fp8 != nullptr, ta,
+                                    (int64_t)h.items.size(), stream);
     if (st != (int)hipSuccess)
         return hip_fail((hipError_t)st, "tile kernel launch");
     if (!h.merges.empty()) {
@@ -439,6 +454,26 @@ int rp_run_paged(const rp_plan *p, const void *q, const void *k_pages, const voi
 {
     PagedKV pk{block_table, max_blocks_per_seq, page_size};
     return run_plan(p, q, k_pages, v_pages, o, lse, sm_scale, workspace, workspace_bytes, stream, &pk);
+}
+
+int rp_run_fp8kv(const rp_plan *p, const void *q, const void *k_fp8, const void *v_fp8, float k_scale,
+                 float v_scale, void *o, float *lse, float sm_scale, void *workspace,
+                 size_t workspace_bytes, void *stream)
+{
+    Fp8KV f{k_scale, v_scale};
+    return run_plan(p, q, k_fp8, v_fp8, o, lse, sm_scale, workspace, workspace_bytes, stream, nullptr,
+                    false, &f);
+}
+
+int rp_run_paged_fp8kv(const rp_plan *p, const void *q, const void *k_pages, const void *v_pages,
+                       const int32_t *block_table, int max_blocks_per_seq, int page_size,
+                       float k_scale, float v_scale, void *o, float *lse, float sm_scale,
+                       void *workspace, size_t workspace_bytes, void *stream)
+{
+    PagedKV pk{block_table, max_blocks_per_seq, page_size};
+    Fp8KV f{k_scale, v_scale};
+    return run_plan(p, q, k_pages, v_pages, o, lse, sm_scale, workspace, workspace_bytes, stream, &pk,
+                    false, &f);
 }
 
 void rp_plan_destroy(rp_plan *p) { free_plan(p); }

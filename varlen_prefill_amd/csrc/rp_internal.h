@@ -109,6 +109,9 @@ struct TileArgs {
     const int32_t *block_table;
     int32_t max_blocks;
     int32_t page_shift;    // log2(page_size)
+    // FP8 K/V (the fp8 kernel only): k and v hold e4m3 bytes; O is scaled by
+    // v_scale (k_scale is folded into scale_log2 by the host)
+    float v_scale;
 };
 
 struct MergeArgs {
@@ -122,7 +125,8 @@ struct MergeArgs {
 };
 
 // Host-side launchers (defined in the .hip file).  Return a hipError_t value.
-int launch_tile_kernel(int head_dim, bool paged, const TileArgs &args, int64_t num_items, void *stream);
+int launch_tile_kernel(int head_dim, bool paged, bool fp8, const TileArgs &args, int64_t num_items,
+                       void *stream);
 int launch_merge_kernel(int head_dim, const MergeArgs &args, int64_t num_items, void *stream);
 
 }  // namespace rp

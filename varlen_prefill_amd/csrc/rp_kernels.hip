@@ -284,9 +284,10 @@ __device__ __attribute__((always_inline)) inline void block_step(
             }
 }
 
-template <int HD, bool POS_SCALE, bool PAGED>
+template <int HD, bool POS_SCALE, bool PAGED, bool FP8>
 __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
 {
+    static_assert(!FP8 || HD == 128, "FP8 K/V is implemented for head_dim 128");
     using T = Tile<HD>;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -435,6 +436,58 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     };
 
+    // FP8 K/V (e4m3 bytes): each wave moves 8 key rows of K and of V (1 KB
+    // each, whole 128-byte rows) into its own staging slot after the bf16
+    // stages, then converts the bytes it loaded itself to bf16 (exactly:
+    // every e4m3 value is a bf16 value) and writes them into the block's
+    // stage in the bf16 layout, so the block computation is unchanged.  The
+    // dequantisation scales are folded into the softmax scale (k_scale) and
+    // the final normalisation (v_scale).  A wave's 8 rows are aligned
+    // consecutive keys, so paging keeps one page id per wave and block.
+    auto issue_fp8 = [&](int kb) __attribute__((always_inline)) {
+        const int kv_stride_b = a.num_kv_heads * HD;   // bytes between fp8 key rows
+        const size_t head_b = ((size_t)(PAGED ? 0 : it.kv_row0) * a.num_kv_heads + it.kv_head) * HD;
+        const int f8_row = wu * 8 + (lane >> 3);        // this lane's key row in the block
+        const int f8_chunk = lane & 7;                   // its 16-byte chunk (16 elements)
+        const size_t blk = PAGED ? ((size_t)__builtin_amdgcn_readfirstlane(max(pg_next, 0)) << a.page_shift) * kv_stride_b
+                                 : (size_t)kb * T::BK * kv_stride_b;
+        const char *kp = static_cast<const char *>(a.k) + head_b + blk;
+        const char *vp = static_cast<const char *>(a.v) + head_b + blk;
+        int row = min(f8_row, it.kv_len - 1 - kb * T::BK);
+        if (PAGED)
+            row = (kb * T::BK + row) & page_mask;
+        const unsigned off = (unsigned)(row * kv_stride_b + 16 * f8_chunk);
+        const unsigned dst = lds_base + (unsigned)(T::STAGES * T::STAGE_BYTES + wu * 1024);
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :: "s"(dst), "v"(off), "s"(kp) : "memory", "m0");
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :: "s"(dst + 4096u), "v"(off), "s"(vp) : "memory", "m0");
+    };
+    auto convert_fp8 = [&](int buf) __attribute__((always_inline)) {
+        typedef __bf16 bf16x2e __attribute__((ext_vector_type(2)));
+        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+        const int f8_row = wu * 8 + (lane >> 3);
+        const int f8_chunk = lane & 7;
+        const char *src = smem + T::STAGES * T::STAGE_BYTES + wu * 1024 + 16 * lane;
+        const u32x4 kq = *reinterpret_cast<const u32x4 *>(src);
+        const u32x4 vq = *reinterpret_cast<const u32x4 *>(src + 4096);
+        auto cvt8 = [](unsigned x, unsigned y) __attribute__((always_inline)) {
+            u32x4 u;
+            u[0] = __builtin_bit_cast(unsigned, (bf16x2e)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false));
+            u[1] = __builtin_bit_cast(unsigned, (bf16x2e)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true));
+            u[2] = __builtin_bit_cast(unsigned, (bf16x2e)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y, 1.0f, false));
+            u[3] = __builtin_bit_cast(unsigned, (bf16x2e)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y, 1.0f, true));
+            return __builtin_bit_cast(bf16x8, u);
+        };
+        char *Kd = smem + buf * T::STAGE_BYTES + f8_row * T::RB;
+        char *Vd = Kd + T::TILE_BYTES;
+        const int c0 = 2 * f8_chunk;
+        *reinterpret_cast<bf16x8 *>(Kd + 16 * (c0 ^ swz_k(f8_row))) = cvt8(kq[0], kq[1]);
+        *reinterpret_cast<bf16x8 *>(Kd + 16 * ((c0 + 1) ^ swz_k(f8_row))) = cvt8(kq[2], kq[3]);
+        *reinterpret_cast<bf16x8 *>(Vd + 16 * (c0 ^ swz_v(f8_row))) = cvt8(vq[0], vq[1]);
+        *reinterpret_cast<bf16x8 *>(Vd + 16 * ((c0 + 1) ^ swz_v(f8_row))) = cvt8(vq[2], vq[3]);
+    };
+
     // The first blocks' K/V loads go out before the Q loads so that the
     // latencies overlap.  Block kb lives in stage kb % STAGES (absolute block
     // parity, so that the unrolled loop below knows every stage at compile
@@ -443,7 +496,10 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
     for (int kb = kb_begin; kb < kb_pre; ++kb) {
         if (PAGED)
             page_id(kb);
-        issue_loads(kb, HD == 128 ? kb % T::STAGES : kb - kb_begin);
+        if (FP8)
+            issue_fp8(kb);
+        else
+            issue_loads(kb, HD == 128 ? kb % T::STAGES : kb - kb_begin);
     }
     if (PAGED && kb_pre < kb_end)
         page_id(kb_pre);
@@ -478,6 +534,8 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
     st.l = 0.0f;
 
     wait_loads(kb_pre - kb_begin - 1);
+    if (FP8 && kb_begin < kb_end)
+        convert_fp8(kb_begin % T::STAGES);
     __syncthreads();
 
     // Blocks below the first row's causal limit need no mask; they come
@@ -509,7 +567,10 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
         auto step = [&](int kb, auto buf_tag) __attribute__((always_inline)) {
             constexpr int BUF = decltype(buf_tag)::value;
             if (kb + 1 < kb_end) {
-                issue_loads(kb + 1, BUF ^ 1);
+                if (FP8)
+                    issue_fp8(kb + 1);
+                else
+                    issue_loads(kb + 1, BUF ^ 1);
                 // the page ids of the block loaded next iteration
                 if (PAGED && kb + 2 < kb_end)
                     page_id(kb + 2);
@@ -519,6 +580,8 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
             const int thr = lim_row - kb * T::BK - 4 * h;
             block_step<HD, POS_SCALE, MASK, HILO>(st, Ks, Vs, c, thr, qc, h, grp, s16);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // block kb + 1 has landed
+            if (FP8 && kb + 1 < kb_end)
+                convert_fp8(BUF ^ 1);
             __syncthreads();
         };
         int kb = kb_from;
@@ -553,7 +616,7 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
 
     // ---- epilogue ----
     const float lt = pair_sum(st.l);
-    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    const float inv = lt > 0.0f ? (FP8 ? a.v_scale : 1.0f) / lt : 0.0f;
     const float lse2 = lt > 0.0f ? st.m + log2f(lt) : -INFINITY;
     // The outputs go out through LDS (the K/V stages are free after the last
     // block barrier; each wave uses its own region): the wave writes its
@@ -632,7 +695,7 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
     }
 }
 
-template <int HD, bool PAGED>
+template <int HD, bool PAGED, bool FP8>
 __global__ __launch_bounds__(kThreads, HD == 128 ? 2 : 1) void tile_kernel(TileArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -640,10 +703,14 @@ __global__ __launch_bounds__(kThreads, HD == 128 ? 2 : 1) void tile_kernel(TileA
     if (it.n_tok == 0)
         return;  // padding item of the launch order
     if (a.scale_log2 > 0.0f)
-        tile_body<HD, true, PAGED>(a, it, smem);
+        tile_body<HD, true, PAGED, FP8>(a, it, smem);
     else
-        tile_body<HD, false, PAGED>(a, it, smem);
+        tile_body<HD, false, PAGED, FP8>(a, it, smem);
 }
+
+// dynamic LDS of a tile kernel instance: the K/V stages, plus the fp8 staging slots
+template <int HD, bool FP8>
+constexpr int tile_lds_bytes() { return Tile<HD>::LDS_BYTES + (FP8 ? 2 * Tile<HD>::BK * HD : 0); }
 
 template <int HD>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a)
@@ -684,36 +751,42 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a)
     }
 }
 
-template <int HD, bool PAGED>
+template <int HD, bool PAGED, bool FP8>
 int launch_tile(const TileArgs &args, int64_t num_items, hipStream_t stream)
 {
+    constexpr int lds = tile_lds_bytes<HD, FP8>();
+    const void *fn = reinterpret_cast<const void *>(&tile_kernel<HD, PAGED, FP8>);
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&tile_kernel<HD, PAGED>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           Tile<HD>::LDS_BYTES);
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess)
             return (int)e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((tile_kernel<HD, PAGED>), dim3((unsigned)num_items), dim3(kThreads),
-                       Tile<HD>::LDS_BYTES, stream, args);
+    auto kernel = tile_kernel<HD, PAGED, FP8>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)num_items), dim3(kThreads), lds, stream, args);
     return (int)hipGetLastError();
 }
 
 }  // namespace
 
-int launch_tile_kernel(int head_dim, bool paged, const TileArgs &args, int64_t num_items, void *stream)
+int launch_tile_kernel(int head_dim, bool paged, bool fp8, const TileArgs &args, int64_t num_items,
+                       void *stream)
 {
     if (num_items <= 0)
         return (int)hipSuccess;
     if (num_items > INT_MAX)
         return (int)hipErrorInvalidValue;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (head_dim == 128 && fp8)
+        return paged ? launch_tile<128, true, true>(args, num_items, s)
+                     : launch_tile<128, false, true>(args, num_items, s);
     if (head_dim == 128)
-        return paged ? launch_tile<128, true>(args, num_items, s) : launch_tile<128, false>(args, num_items, s);
-    if (head_dim == 256)
-        return paged ? launch_tile<256, true>(args, num_items, s) : launch_tile<256, false>(args, num_items, s);
+        return paged ? launch_tile<128, true, false>(args, num_items, s)
+                     : launch_tile<128, false, false>(args, num_items, s);
+    if (head_dim == 256 && !fp8)
+        return paged ? launch_tile<256, true, false>(args, num_items, s)
+                     : launch_tile<256, false, false>(args, num_items, s);
     return (int)hipErrorInvalidValue;
 }
 

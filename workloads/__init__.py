@@ -12,7 +12,8 @@ Layout (the packed "NHD" layout of the FlashInfer ragged prefill API, page
 """
 
 from .configs import CONFIGS, WorkloadConfig, get_config
-from .gen import PagedKV, RaggedBatch, make_batch, make_config_batch, make_paged, request_tensors
+from .gen import (PagedKV, RaggedBatch, make_batch, make_config_batch, make_fp8_kv, make_paged,
+                  request_tensors)
 
 __all__ = [
     "CONFIGS",
@@ -24,4 +25,5 @@ __all__ = [
     "request_tensors",
     "PagedKV",
     "make_paged",
+    "make_fp8_kv",
 ]

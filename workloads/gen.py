@@ -121,7 +121,8 @@ class PagedKV:
 
 
 def make_paged(batch: RaggedBatch, page_size: int, seed: int, spare_pages: int = 3,
-               spare_columns: int = 2) -> PagedKV:
+               spare_columns: int = 2, k: Optional[torch.Tensor] = None,
+               v: Optional[torch.Tensor] = None) -> PagedKV:
     """Scatter each request's keys into pages of ``page_size`` keys at random
     physical positions of a pool.
 
@@ -130,6 +131,8 @@ def make_paged(batch: RaggedBatch, page_size: int, seed: int, spare_pages: int =
     pool has ``spare_pages`` pages no request uses (NaN as well).  Table
     columns past a request's pages hold padding: -1, 0 or a stale id of
     another page, drawn at random.  None of this padding may change a result.
+    ``k``/``v`` replace the batch's K/V (e.g. uint8 FP8 E4M3 codes of the same
+    shape); unused slots then hold the E4M3 NaN code 0x7f.
     """
     rng = np.random.default_rng([seed, 7919, page_size])
     kv_lens = np.diff(batch.kv_indptr).astype(np.int64)
@@ -137,8 +140,11 @@ def make_paged(batch: RaggedBatch, page_size: int, seed: int, spare_pages: int =
     n_pages = int(need.sum()) + spare_pages
     perm = rng.permutation(n_pages)
     hkv, d = batch.num_kv_heads, batch.head_dim
-    kp = torch.full((max(n_pages, 1), page_size, hkv, d), float("nan"), dtype=torch.bfloat16)
-    vp = torch.full((max(n_pages, 1), page_size, hkv, d), float("nan"), dtype=torch.bfloat16)
+    src_k = batch.k if k is None else k
+    src_v = batch.v if v is None else v
+    fill = float("nan") if src_k.dtype == torch.bfloat16 else 0x7F
+    kp = torch.full((max(n_pages, 1), page_size, hkv, d), fill, dtype=src_k.dtype)
+    vp = torch.full((max(n_pages, 1), page_size, hkv, d), fill, dtype=src_v.dtype)
     max_blocks = int(need.max() if len(need) else 0) + spare_columns
     table = np.zeros((batch.batch, max(max_blocks, 1)), dtype=np.int32)
     nxt = 0
@@ -150,9 +156,18 @@ def make_paged(batch: RaggedBatch, page_size: int, seed: int, spare_pages: int =
             table[b, p] = phys
             lo = p * page_size
             hi = min(lo + page_size, int(kv_lens[b]))
-            kp[phys, : hi - lo] = batch.k[base + lo: base + hi]
-            vp[phys, : hi - lo] = batch.v[base + lo: base + hi]
+            kp[phys, : hi - lo] = src_k[base + lo: base + hi]
+            vp[phys, : hi - lo] = src_v[base + lo: base + hi]
         pad = rng.integers(0, 3, table.shape[1] - int(need[b]))
         stale = rng.integers(0, max(n_pages, 1), pad.size)
         table[b, int(need[b]):] = np.where(pad == 0, -1, np.where(pad == 1, 0, stale))
     return PagedKV(k_pages=kp, v_pages=vp, block_table=table, page_size=page_size)
+
+
+def make_fp8_kv(batch: RaggedBatch, k_scale: float, v_scale: float):
+    """FP8 (OCP E4M3) codes of the batch's K and V: K / k_scale and V / v_scale
+    rounded to the nearest E4M3 value (torch's float8_e4m3fn conversion),
+    returned as uint8 tensors of the same shape (CPU)."""
+    k8 = (batch.k.float() / k_scale).to(torch.float8_e4m3fn).view(torch.uint8)
+    v8 = (batch.v.float() / v_scale).to(torch.float8_e4m3fn).view(torch.uint8)
+    return k8, v8
