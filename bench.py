@@ -372,10 +372,13 @@ def main():
         causal = cfg.causal and not args.noncausal
         plan = vp.Plan(indptr_from_lens(cfg.qo_lens), indptr_from_lens(cfg.kv_lens),
                        cfg.num_qo_heads, cfg.num_kv_heads, cfg.head_dim, causal, host_only=True)
+        alg = plan.info["bytes"]
+        if args.kv_fp8:
+            alg -= 2.0 * cfg.num_kv_heads * cfg.head_dim * cfg.total_kv   # K/V at one byte
         path = record_traffic(args.record_traffic[0], args.record_traffic[1],
                               cfg.name + ("" if causal else "_noncausal")
-                              + (f"_paged{args.paged}" if args.paged else ""), cfg.head_dim,
-                              plan.info["bytes"])
+                              + ("_fp8kv" if args.kv_fp8 else "")
+                              + (f"_paged{args.paged}" if args.paged else ""), cfg.head_dim, alg)
         print(path)
         return
     import torch
