@@ -198,8 +198,8 @@ int rp_run_paged(const rp_plan *plan, const void *q, const void *k_pages, const 
  * v_scale (per-tensor scales, finite).  Q, O and LSE are as for rp_run (bf16
  * Q and O).  The result is the attention over the dequantised K and V; the
  * E4M3 codes convert to bf16 exactly, k_scale is folded into the softmax
- * scale and v_scale into the output normalisation.  head_dim must be 128
- * (RP_EUNSUPPORTED otherwise).  Codes 0x7f / 0xff (NaN) give NaN. */
+ * scale and v_scale into the output normalisation.  Both head dims of the
+ * plan (128, 256) are supported.  Codes 0x7f / 0xff (NaN) give NaN. */
 int rp_run_fp8kv(const rp_plan *plan, const void *q, const void *k_fp8, const void *v_fp8,
                  float k_scale, float v_scale, void *o, float *lse, float sm_scale,
                  void *workspace, size_t workspace_bytes, void *stream);

@@ -1,4 +1,4 @@
-"""FP8 (OCP E4M3) K/V on the GPU (rp_run_fp8kv, rp_run_paged_fp8kv).
+"""FP8 (OCP E4M3) K/V on the GPU (rp_run_fp8kv, rp_run_paged_fp8kv), head_dim 128 and 256.
 
 Parity against the fp64 FP8 oracle (dequantised K/V, attention by its
 definition) with the standard gates; with unit scales the FP8 path must give
@@ -53,12 +53,16 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", range(len(CASES)))
-def test_fp8_parity(case):
+# head_dim 256 runs the cases whose oracle stays quick at twice the width
+CASES_256 = [0, 2, 3, 4]
+
+
+@pytest.mark.parametrize("d,case", [(128, c) for c in range(len(CASES))] + [(256, c) for c in CASES_256])
+def test_fp8_parity(d, case):
     qo, kv, hq, hkv, causal, ks, vs, chunk = CASES[case]
-    b = make_batch(qo, kv, hq, hkv, 128, seed=5000 + case, q_base=2)
+    b = make_batch(qo, kv, hq, hkv, d, seed=5000 + case + d, q_base=2)
     k8, v8 = make_fp8_kv(b, ks, vs)
-    sm = default_scale(128)
+    sm = default_scale(d)
     plan = _plan(b, causal, kv_chunk=chunk)
     q, o, lse = _outs(b)
     plan.run_fp8kv(q, k8.to(DEV), v8.to(DEV), ks, vs, out=o, lse=lse, sm_scale=sm)
@@ -71,13 +75,13 @@ def test_fp8_parity(case):
     assert torch.isnan(o[:2]).all() and torch.isnan(lse[:2]).all()
 
 
-@pytest.mark.parametrize("causal", [True, False])
-def test_fp8_unit_scales_equal_bf16_kernel_bitwise(causal):
-    b = make_batch([1, 130, 257, 64, 40], [1, 300, 257, 64, 900], 32, 8, 128, seed=5100)
+@pytest.mark.parametrize("d,causal", [(128, True), (128, False), (256, True), (256, False)])
+def test_fp8_unit_scales_equal_bf16_kernel_bitwise(d, causal):
+    b = make_batch([1, 130, 257, 64, 40], [1, 300, 257, 64, 900], 32, 8, d, seed=5100 + d)
     k8, v8 = make_fp8_kv(b, 1.0, 1.0)
     kb = k8.view(torch.float8_e4m3fn).to(torch.bfloat16)
     vb = v8.view(torch.float8_e4m3fn).to(torch.bfloat16)
-    sm = default_scale(128)
+    sm = default_scale(d)
     plan = _plan(b, causal, kv_chunk=256)
     q, o, lse = _outs(b)
     plan.run_fp8kv(q, k8.to(DEV), v8.to(DEV), 1.0, 1.0, out=o, lse=lse, sm_scale=sm)
@@ -88,12 +92,12 @@ def test_fp8_unit_scales_equal_bf16_kernel_bitwise(causal):
     assert torch.equal(lse.view(torch.int32), lb.view(torch.int32))
 
 
-@pytest.mark.parametrize("page_size", [16, 64])
-def test_fp8_paged_equals_contiguous_bitwise(page_size):
-    b = make_batch([33, 129, 7, 1], [500, 129, 2, 2000], 16, 2, 128, seed=5200 + page_size)
+@pytest.mark.parametrize("d,page_size", [(128, 16), (128, 64), (256, 16)])
+def test_fp8_paged_equals_contiguous_bitwise(d, page_size):
+    b = make_batch([33, 129, 7, 1], [500, 129, 2, 2000], 16, 2, d, seed=5200 + page_size + d)
     k8, v8 = make_fp8_kv(b, 0.5, 2.0)
     pk = make_paged(b, page_size, seed=5200 + page_size, k=k8, v=v8)
-    sm = default_scale(128)
+    sm = default_scale(d)
     plan = _plan(b, True)
     q, o, lse = _outs(b)
     plan.run_paged_fp8kv(q, pk.k_pages.to(DEV), pk.v_pages.to(DEV),
@@ -111,8 +115,8 @@ def test_fp8_argument_errors():
     b = make_batch([20], [40], 4, 2, 256, seed=5300)
     plan = _plan(b, True)
     q = b.q.to(DEV)
-    k8 = torch.zeros(40, 2, 256, dtype=torch.uint8, device=DEV)
-    with pytest.raises(vp.RaggedPrefillError, match="head_dim 128"):
+    k8 = torch.zeros(40, 2, 128, dtype=torch.uint8, device=DEV)   # head_dim of another plan
+    with pytest.raises(ValueError, match="256"):
         plan.run_fp8kv(q, k8, k8, 1.0, 1.0)
     plan.close()
     b = make_batch([20], [40], 4, 2, 128, seed=5301)

@@ -217,7 +217,7 @@ class Plan:
                   stream=None):
         """Run with FP8 (OCP E4M3) K/V: k_fp8, v_fp8 uint8 (or float8_e4m3fn)
         [rows_kv, num_kv_heads, head_dim] on the GPU, dequantised as code x
-        k_scale / code x v_scale (head_dim 128)."""
+        k_scale / code x v_scale."""
         rows_q = int(self.q_indptr[-1])
         rows_kv = int(self.kv_indptr[-1])
         _check_tensor(q, "q", rows_q, self.num_qo_heads, self.head_dim)
@@ -238,7 +238,7 @@ class Plan:
                         out=None, lse=None, sm_scale: Optional[float] = None,
                         return_lse: bool = True, workspace=None, stream=None):
         """run_paged with FP8 (OCP E4M3) page pools [num_pages, page_size,
-        num_kv_heads, head_dim] (uint8 or float8_e4m3fn), head_dim 128."""
+        num_kv_heads, head_dim] (uint8 or float8_e4m3fn)."""
         import torch
         rows_q = int(self.q_indptr[-1])
         _check_tensor(q, "q", rows_q, self.num_qo_heads, self.head_dim)

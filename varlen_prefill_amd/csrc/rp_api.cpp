@@ -250,8 +250,6 @@ int run_plan(const rp_plan *p, const void *q, const void *k, const void *v, void
     if (fp8) {
         if (!std::isfinite(fp8->k_scale) || !std::isfinite(fp8->v_scale))
             return fail(RP_EINVAL, "k_scale and v_scale must be finite");
-        if (h.shape.head_dim != 128)
-            return fail(RP_EUNSUPPORTED, "FP8 K/V is implemented for head_dim 128 only");
     }
     if (h.items.empty())
         return RP_OK;  // empty batch / no query rows: nothing to launch

@@ -287,7 +287,6 @@ __device__ __attribute__((always_inline)) inline void block_step(
 template <int HD, bool POS_SCALE, bool PAGED, bool FP8>
 __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
 {
-    static_assert(!FP8 || HD == 128, "FP8 K/V is implemented for head_dim 128");
     using T = Tile<HD>;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -436,41 +435,43 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     };
 
-    // FP8 K/V (e4m3 bytes): each wave moves 8 key rows of K and of V (1 KB
-    // each, whole 128-byte rows) into its own staging slot after the bf16
-    // stages, then converts the bytes it loaded itself to bf16 (exactly:
-    // every e4m3 value is a bf16 value) and writes them into the block's
-    // stage in the bf16 layout, so the block computation is unchanged.  The
-    // dequantisation scales are folded into the softmax scale (k_scale) and
-    // the final normalisation (v_scale).  A wave's 8 rows are aligned
-    // consecutive keys, so paging keeps one page id per wave and block.
+    // FP8 K/V (e4m3 bytes): each wave moves 8 key rows of K and of V (whole
+    // rows of HD bytes, 64 lanes x 16 bytes per load) into its own staging
+    // slot after the bf16 stages, then converts the bytes it loaded itself to
+    // bf16 (exactly: every e4m3 value is a bf16 value) and writes them into
+    // the block's stage in the bf16 layout, so the block computation is
+    // unchanged.  The dequantisation scales are folded into the softmax
+    // scale (k_scale) and the final normalisation (v_scale).  A wave's 8
+    // rows are aligned consecutive keys, so paging keeps one page id per
+    // wave and block.  Staging: K of wave w at 8 HD w, V at BK HD + 8 HD w.
+    constexpr int F8_CPR = HD / 16;            // 16-byte chunks per fp8 row
+    constexpr int F8_RPL = 64 / F8_CPR;        // rows per load instruction
+    constexpr int F8_NL = 8 / F8_RPL;          // load instructions per wave and tensor
     auto issue_fp8 = [&](int kb) __attribute__((always_inline)) {
         const int kv_stride_b = a.num_kv_heads * HD;   // bytes between fp8 key rows
         const size_t head_b = ((size_t)(PAGED ? 0 : it.kv_row0) * a.num_kv_heads + it.kv_head) * HD;
-        const int f8_row = wu * 8 + (lane >> 3);        // this lane's key row in the block
-        const int f8_chunk = lane & 7;                   // its 16-byte chunk (16 elements)
         const size_t blk = PAGED ? ((size_t)__builtin_amdgcn_readfirstlane(max(pg_next, 0)) << a.page_shift) * kv_stride_b
                                  : (size_t)kb * T::BK * kv_stride_b;
         const char *kp = static_cast<const char *>(a.k) + head_b + blk;
         const char *vp = static_cast<const char *>(a.v) + head_b + blk;
-        int row = min(f8_row, it.kv_len - 1 - kb * T::BK);
-        if (PAGED)
-            row = (kb * T::BK + row) & page_mask;
-        const unsigned off = (unsigned)(row * kv_stride_b + 16 * f8_chunk);
-        const unsigned dst = lds_base + (unsigned)(T::STAGES * T::STAGE_BYTES + wu * 1024);
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-                     :: "s"(dst), "v"(off), "s"(kp) : "memory", "m0");
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-                     :: "s"(dst + 4096u), "v"(off), "s"(vp) : "memory", "m0");
+#pragma unroll
+        for (int i = 0; i < F8_NL; ++i) {
+            const int f8_row = wu * 8 + i * F8_RPL + lane / F8_CPR;   // this lane's key row in the block
+            const int f8_chunk = lane % F8_CPR;                         // its 16-byte chunk (16 elements)
+            int row = min(f8_row, it.kv_len - 1 - kb * T::BK);
+            if (PAGED)
+                row = (kb * T::BK + row) & page_mask;
+            const unsigned off = (unsigned)(row * kv_stride_b + 16 * f8_chunk);
+            const unsigned dst = lds_base + (unsigned)(T::STAGES * T::STAGE_BYTES + wu * 8 * HD + i * 1024);
+            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                         :: "s"(dst), "v"(off), "s"(kp) : "memory", "m0");
+            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                         :: "s"(dst + (unsigned)(T::BK * HD)), "v"(off), "s"(vp) : "memory", "m0");
+        }
     };
     auto convert_fp8 = [&](int buf) __attribute__((always_inline)) {
         typedef __bf16 bf16x2e __attribute__((ext_vector_type(2)));
         typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-        const int f8_row = wu * 8 + (lane >> 3);
-        const int f8_chunk = lane & 7;
-        const char *src = smem + T::STAGES * T::STAGE_BYTES + wu * 1024 + 16 * lane;
-        const u32x4 kq = *reinterpret_cast<const u32x4 *>(src);
-        const u32x4 vq = *reinterpret_cast<const u32x4 *>(src + 4096);
         auto cvt8 = [](unsigned x, unsigned y) __attribute__((always_inline)) {
             u32x4 u;
             u[0] = __builtin_bit_cast(unsigned, (bf16x2e)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false));
@@ -479,13 +480,21 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
             u[3] = __builtin_bit_cast(unsigned, (bf16x2e)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y, 1.0f, true));
             return __builtin_bit_cast(bf16x8, u);
         };
-        char *Kd = smem + buf * T::STAGE_BYTES + f8_row * T::RB;
-        char *Vd = Kd + T::TILE_BYTES;
-        const int c0 = 2 * f8_chunk;
-        *reinterpret_cast<bf16x8 *>(Kd + 16 * (c0 ^ swz_k(f8_row))) = cvt8(kq[0], kq[1]);
-        *reinterpret_cast<bf16x8 *>(Kd + 16 * ((c0 + 1) ^ swz_k(f8_row))) = cvt8(kq[2], kq[3]);
-        *reinterpret_cast<bf16x8 *>(Vd + 16 * (c0 ^ swz_v(f8_row))) = cvt8(vq[0], vq[1]);
-        *reinterpret_cast<bf16x8 *>(Vd + 16 * ((c0 + 1) ^ swz_v(f8_row))) = cvt8(vq[2], vq[3]);
+#pragma unroll
+        for (int i = 0; i < F8_NL; ++i) {
+            const int f8_row = wu * 8 + i * F8_RPL + lane / F8_CPR;
+            const int f8_chunk = lane % F8_CPR;
+            const char *src = smem + T::STAGES * T::STAGE_BYTES + wu * 8 * HD + i * 1024 + 16 * lane;
+            const u32x4 kq = *reinterpret_cast<const u32x4 *>(src);
+            const u32x4 vq = *reinterpret_cast<const u32x4 *>(src + T::BK * HD);
+            char *Kd = smem + buf * T::STAGE_BYTES + f8_row * T::RB;
+            char *Vd = Kd + T::TILE_BYTES;
+            const int c0 = 2 * f8_chunk;
+            *reinterpret_cast<bf16x8 *>(Kd + 16 * (c0 ^ swz_k(f8_row))) = cvt8(kq[0], kq[1]);
+            *reinterpret_cast<bf16x8 *>(Kd + 16 * ((c0 + 1) ^ swz_k(f8_row))) = cvt8(kq[2], kq[3]);
+            *reinterpret_cast<bf16x8 *>(Vd + 16 * (c0 ^ swz_v(f8_row))) = cvt8(vq[0], vq[1]);
+            *reinterpret_cast<bf16x8 *>(Vd + 16 * ((c0 + 1) ^ swz_v(f8_row))) = cvt8(vq[2], vq[3]);
+        }
     };
 
     // The first blocks' K/V loads go out before the Q loads so that the
@@ -535,7 +544,7 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
 
     wait_loads(kb_pre - kb_begin - 1);
     if (FP8 && kb_begin < kb_end)
-        convert_fp8(kb_begin % T::STAGES);
+        convert_fp8(HD == 128 ? kb_begin % T::STAGES : 0);
     __syncthreads();
 
     // Blocks below the first row's causal limit need no mask; they come
@@ -550,8 +559,12 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
             // head_dim 256: stage (kb - kb_begin) % STAGES, one block per iteration
             for (int kb = kb_from; kb < kb_to; ++kb) {
                 const int buf = (kb - kb_begin) % T::STAGES;
-                if (kb + T::STAGES - 1 < kb_end) {
-                    issue_loads(kb + T::STAGES - 1, (kb + T::STAGES - 1 - kb_begin) % T::STAGES);
+                const int kb_next = kb + T::STAGES - 1;
+                if (kb_next < kb_end) {
+                    if (FP8)
+                        issue_fp8(kb_next);
+                    else
+                        issue_loads(kb_next, (kb_next - kb_begin) % T::STAGES);
                     if (PAGED && kb + T::STAGES < kb_end)
                         page_id(kb + T::STAGES);
                 }
@@ -560,6 +573,10 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
                 const int thr = lim_row - kb * T::BK - 4 * h;
                 block_step<HD, POS_SCALE, MASK, HILO>(st, Ks, Vs, c, thr, qc, h, grp, s16);
                 wait_loads(min(kb_end, kb + T::STAGES) - (kb + 2));
+                // fp8: the staging slot holds one block, so two stages keep
+                // one block in flight, converted here
+                if (FP8 && kb_next < kb_end)
+                    convert_fp8((kb_next - kb_begin) % T::STAGES);
                 __syncthreads();
             }
             return;
@@ -784,7 +801,10 @@ int launch_tile_kernel(int head_dim, bool paged, bool fp8, const TileArgs &args,
     if (head_dim == 128)
         return paged ? launch_tile<128, true, false>(args, num_items, s)
                      : launch_tile<128, false, false>(args, num_items, s);
-    if (head_dim == 256 && !fp8)
+    if (head_dim == 256 && fp8)
+        return paged ? launch_tile<256, true, true>(args, num_items, s)
+                     : launch_tile<256, false, true>(args, num_items, s);
+    if (head_dim == 256)
         return paged ? launch_tile<256, true, false>(args, num_items, s)
                      : launch_tile<256, false, false>(args, num_items, s);
     return (int)hipErrorInvalidValue;
