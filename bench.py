@@ -136,8 +136,13 @@ def cpu_baseline(batch, cfg, causal: bool, sm_scale: float, target_s: float) -> 
         flops = float(np.sum(4.0 * cfg.head_dim * lim[toks]))
         return n, dt, flops
 
-    n, dt, _ = run(256)                       # calibration
-    n_target = int(max(256, min(2_000_000, n * target_s / max(dt, 1e-3))))
+    # calibration: grow the sample until a run takes a tenth of the target,
+    # so that fixed start-up costs do not skew the rate it extrapolates from
+    cap = 2_000_000
+    n, dt, _ = run(256)
+    while dt < 0.1 * target_s and n < cap:
+        n, dt, _ = run(min(cap, n * 8))
+    n_target = int(max(256, min(cap, n * target_s / max(dt, 1e-3))))
     n, dt, flops = run(n_target)
     tflops = flops / dt / 1e12
     flops_per_token = 4.0 * cfg.head_dim * cfg.num_qo_heads * float(np.mean(lim))
