@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define RP_ABI_VERSION 4
+#define RP_ABI_VERSION 5
 
 /* Status codes. */
 enum rp_status {
@@ -278,6 +278,21 @@ int rp_run_shared_prefix(const rp_plan *plan, const void *q, const void *k_share
                          const void *v_shared, const void *k_unique, const void *v_unique,
                          void *o, float *lse, float sm_scale, void *workspace,
                          size_t workspace_bytes, void *stream);
+
+/* rp_run_shared_prefix with each request's own keys in a paged cache (the
+ * serving layout of the cascade: page "flashinfer-ai/flashinfer", cascade
+ * API, shared-prefix batch decode/prefill over a paged KV cache): k_pages,
+ * v_pages bf16 [num_pages][page_size][num_kv_heads][head_dim], block_table,
+ * max_blocks_per_seq and page_size as for rp_run_paged (key j of request b
+ * at page block_table[b * max_blocks_per_seq + j / page_size], slot
+ * j % page_size).  The shared prefix stays one contiguous bf16 block, read
+ * once for all requests; everything else as for rp_run_shared_prefix.  The
+ * result is bit-identical to rp_run_shared_prefix on the same keys. */
+int rp_run_shared_prefix_paged(const rp_plan *plan, const void *q, const void *k_shared,
+                               const void *v_shared, const void *k_pages, const void *v_pages,
+                               const int32_t *block_table, int max_blocks_per_seq, int page_size,
+                               void *o, float *lse, float sm_scale, void *workspace,
+                               size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = _lib.load()
-    assert lib.rp_abi_version() == 4
+    assert lib.rp_abi_version() == 5
     for st in (0, -1, -2, -3, -4):
         assert lib.rp_status_string(st)
     assert lib.rp_status_string(12345) == b"unknown status"

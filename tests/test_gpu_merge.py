@@ -8,7 +8,8 @@ summation bound (k + 4) 2^-24 sum_i w_i |v_i| (k fma roundings, the
 exponential, the normalisation); the scale sum_i w_i |v_i| is the oracle's
 merge of |v|.  The LSE must agree within fp32 rounding.  Shared-prefix attention is
 checked against the oracle's attention over the concatenated keys with the
-usual parity gates, and bit for bit against rp_run when the prefix is empty.
+usual parity gates, bit for bit against rp_run when the prefix is empty, and
+with the own keys in a paged cache bit for bit against the contiguous run.
 """
 
 from __future__ import annotations
@@ -19,7 +20,7 @@ import torch
 
 import oracle
 from parity import _bf16_neighbours, bf16_to_f64, compare, default_scale
-from workloads import make_batch, request_tensors
+from workloads import make_batch, make_paged, request_tensors
 
 pytestmark = pytest.mark.gpu
 
@@ -183,6 +184,33 @@ def test_shared_prefix_empty_prefix_is_rp_run_bitwise():
     torch.cuda.synchronize()
     assert torch.equal(o[3:].view(torch.int16), oc[3:].view(torch.int16))
     assert torch.equal(lse[3:].view(torch.int32), lc[3:].view(torch.int32))
+
+
+@pytest.mark.parametrize("case", [
+    # qo, own kv, shared len, Hq, Hkv, D, causal, page size
+    ([30, 130, 1, 0, 64], [30, 200, 5, 9, 64], 700, 32, 8, 128, True, 16),
+    ([17, 90], [17, 300], 1000, 16, 4, 256, True, 64),
+    ([5, 64, 40], [0, 64, 333], 33, 8, 2, 128, False, 32),
+])
+def test_shared_prefix_paged_equals_contiguous_bitwise(case):
+    """Own keys in a paged cache (random page order, padded table) give the
+    same bits as the contiguous own keys."""
+    import varlen_prefill_amd as vp
+    qo, kv, p, hq, hkv, d, causal, ps = case
+    b = make_batch(qo, kv, hq, hkv, d, seed=800 + p)
+    _, ks, vs = request_tensors(800 + p, 10**6, 0, p, hq, hkv, d)
+    pk = make_paged(b, ps, seed=800 + ps)
+    sm = default_scale(d)
+    plan = vp.SharedPrefixPlan(b.q_indptr, b.kv_indptr, p, hq, hkv, d, causal)
+    q, ksd, vsd = b.q.to(DEV), ks.to(DEV), vs.to(DEV)
+    oc, lc = plan.run(q, ksd, vsd, b.k.to(DEV), b.v.to(DEV), sm_scale=sm)
+    oc, lc = oc.clone(), lc.clone()
+    op, lp = plan.run_paged(q, ksd, vsd, pk.k_pages.to(DEV), pk.v_pages.to(DEV),
+                            torch.from_numpy(pk.block_table).to(DEV), sm_scale=sm)
+    torch.cuda.synchronize()
+    plan.close()
+    assert torch.equal(op.view(torch.int16), oc.view(torch.int16))
+    assert torch.equal(lp.view(torch.int32), lc.view(torch.int32))
 
 
 def test_argument_errors():

@@ -274,21 +274,8 @@ class Plan:
         import torch
         rows_q = int(self.q_indptr[-1])
         _check_tensor(q, "q", rows_q, self.num_qo_heads, self.head_dim)
-        for name, t in (("k_pages", k_pages), ("v_pages", v_pages)):
-            if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dtype != torch.bfloat16:
-                raise TypeError(f"{name} must be a bf16 GPU tensor")
-            if t.dim() != 4 or t.shape[2] != self.num_kv_heads or t.shape[3] != self.head_dim:
-                raise ValueError(f"{name} must be [num_pages, page_size, {self.num_kv_heads}, "
-                                 f"{self.head_dim}], got {tuple(t.shape)}")
-            if not t.is_contiguous():
-                raise ValueError(f"{name} must be contiguous")
-        if k_pages.shape != v_pages.shape:
-            raise ValueError("k_pages and v_pages must have the same shape")
+        _check_pages(k_pages, v_pages, block_table, self.batch, self.num_kv_heads, self.head_dim)
         page_size = int(k_pages.shape[1])
-        if (not isinstance(block_table, torch.Tensor) or block_table.device.type != "cuda"
-                or block_table.dtype != torch.int32 or block_table.dim() != 2
-                or block_table.shape[0] != self.batch or not block_table.is_contiguous()):
-            raise ValueError(f"block_table must be a contiguous int32 [{self.batch}, max_blocks] GPU tensor")
         if out is None:
             out = torch.empty_like(q)
         else:
@@ -367,13 +354,50 @@ class SharedPrefixPlan(Plan):
     def run(self, q, k_shared, v_shared, k_unique, v_unique, out=None, lse=None,
             sm_scale: Optional[float] = None, return_lse: bool = True, workspace=None,
             stream=None):
-        import torch
         rows_q = int(self.q_indptr[-1])
         _check_tensor(q, "q", rows_q, self.num_qo_heads, self.head_dim)
         _check_tensor(k_shared, "k_shared", self.shared_kv_len, self.num_kv_heads, self.head_dim)
         _check_tensor(v_shared, "v_shared", self.shared_kv_len, self.num_kv_heads, self.head_dim)
         _check_tensor(k_unique, "k_unique", int(self.kv_indptr[-1]), self.num_kv_heads, self.head_dim)
         _check_tensor(v_unique, "v_unique", int(self.kv_indptr[-1]), self.num_kv_heads, self.head_dim)
+        out, lse, ws_ptr, ws_bytes, scale = self._shared_outputs(q, out, lse, return_lse, workspace,
+                                                                 sm_scale)
+        st = self._lib.rp_run_shared_prefix(
+            self.handle, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_shared.data_ptr()),
+            ctypes.c_void_p(v_shared.data_ptr()), ctypes.c_void_p(k_unique.data_ptr()),
+            ctypes.c_void_p(v_unique.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+            ctypes.c_void_p(lse.data_ptr()) if lse is not None else None, ctypes.c_float(scale),
+            ws_ptr, ws_bytes, _stream_handle(stream))
+        _lib.check(st, "rp_run_shared_prefix")
+        return out, lse
+
+    def run_paged(self, q, k_shared, v_shared, k_pages, v_pages, block_table, out=None, lse=None,
+                  sm_scale: Optional[float] = None, return_lse: bool = True, workspace=None,
+                  stream=None):
+        """run() with each request's own keys in a paged cache: k_pages,
+        v_pages bf16 [num_pages, page_size, num_kv_heads, head_dim] and
+        block_table int32 [batch, max_blocks] on the GPU, as for Plan.run_paged;
+        the shared prefix stays contiguous."""
+        rows_q = int(self.q_indptr[-1])
+        _check_tensor(q, "q", rows_q, self.num_qo_heads, self.head_dim)
+        _check_tensor(k_shared, "k_shared", self.shared_kv_len, self.num_kv_heads, self.head_dim)
+        _check_tensor(v_shared, "v_shared", self.shared_kv_len, self.num_kv_heads, self.head_dim)
+        _check_pages(k_pages, v_pages, block_table, self.batch, self.num_kv_heads, self.head_dim)
+        out, lse, ws_ptr, ws_bytes, scale = self._shared_outputs(q, out, lse, return_lse, workspace,
+                                                                 sm_scale)
+        st = self._lib.rp_run_shared_prefix_paged(
+            self.handle, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_shared.data_ptr()),
+            ctypes.c_void_p(v_shared.data_ptr()), ctypes.c_void_p(k_pages.data_ptr()),
+            ctypes.c_void_p(v_pages.data_ptr()), ctypes.c_void_p(block_table.data_ptr()),
+            int(block_table.shape[1]), int(k_pages.shape[1]), ctypes.c_void_p(out.data_ptr()),
+            ctypes.c_void_p(lse.data_ptr()) if lse is not None else None, ctypes.c_float(scale),
+            ws_ptr, ws_bytes, _stream_handle(stream))
+        _lib.check(st, "rp_run_shared_prefix_paged")
+        return out, lse
+
+    def _shared_outputs(self, q, out, lse, return_lse, workspace, sm_scale):
+        import torch
+        rows_q = int(self.q_indptr[-1])
         if out is None:
             out = torch.empty_like(q)
         else:
@@ -390,17 +414,25 @@ class SharedPrefixPlan(Plan):
         ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
         scale = _default_scale(self.head_dim) if sm_scale is None else float(sm_scale)
-        st = self._lib.rp_run_shared_prefix(
-            self.handle, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_shared.data_ptr()),
-            ctypes.c_void_p(v_shared.data_ptr()), ctypes.c_void_p(k_unique.data_ptr()),
-            ctypes.c_void_p(v_unique.data_ptr()), ctypes.c_void_p(out.data_ptr()),
-            ctypes.c_void_p(lse.data_ptr()) if lse is not None else None, ctypes.c_float(scale),
-            ws_ptr, ws_bytes, _stream_handle(stream))
-        _lib.check(st, "rp_run_shared_prefix")
-        return out, lse
+        return out, lse, ws_ptr, ws_bytes, scale
 
-    def run_paged(self, *args, **kwargs):
-        raise RaggedPrefillError(-1, "a shared-prefix plan runs through run()")
+
+def _check_pages(k_pages, v_pages, block_table, batch: int, heads: int, head_dim: int) -> None:
+    import torch
+    for name, t in (("k_pages", k_pages), ("v_pages", v_pages)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be a bf16 GPU tensor")
+        if t.dim() != 4 or t.shape[2] != heads or t.shape[3] != head_dim:
+            raise ValueError(f"{name} must be [num_pages, page_size, {heads}, {head_dim}], "
+                             f"got {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if k_pages.shape != v_pages.shape:
+        raise ValueError("k_pages and v_pages must have the same shape")
+    if (not isinstance(block_table, torch.Tensor) or block_table.device.type != "cuda"
+            or block_table.dtype != torch.int32 or block_table.dim() != 2
+            or block_table.shape[0] != batch or not block_table.is_contiguous()):
+        raise ValueError(f"block_table must be a contiguous int32 [{batch}, max_blocks] GPU tensor")
 
 
 def _check_fp8(t, name: str, rows_needed, heads: int, head_dim: int, ndim: int) -> None:

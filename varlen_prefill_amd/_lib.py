@@ -48,6 +48,7 @@ EXPORTS = [
     "rp_merge_states",
     "rp_plan_create_shared_prefix",
     "rp_run_shared_prefix",
+    "rp_run_shared_prefix_paged",
 ]
 
 
@@ -132,6 +133,9 @@ def load():
         lib.rp_run_shared_prefix.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_float, P,
                                              ctypes.c_size_t, P]
         lib.rp_run_shared_prefix.restype = I
+        lib.rp_run_shared_prefix_paged.argtypes = [P, P, P, P, P, P, P, I, I, P, P, ctypes.c_float,
+                                                   P, ctypes.c_size_t, P]
+        lib.rp_run_shared_prefix_paged.restype = I
         _lib = lib
         return lib
 

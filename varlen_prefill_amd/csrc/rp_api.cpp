@@ -520,10 +520,14 @@ int rp_plan_create_shared_prefix(const int32_t *q_indptr, const int32_t *kv_indp
     return RP_OK;
 }
 
-int rp_run_shared_prefix(const rp_plan *p, const void *q, const void *k_shared,
-                         const void *v_shared, const void *k_unique, const void *v_unique, void *o,
-                         float *lse, float sm_scale, void *workspace, size_t workspace_bytes,
-                         void *stream)
+namespace {
+
+// Shared-prefix attention: the shared level, the own-key level (contiguous
+// or paged K/V), then the in-place merge of the two states.
+int run_shared_prefix(const rp_plan *p, const void *q, const void *k_shared, const void *v_shared,
+                      const void *k_own, const void *v_own, const PagedKV *paged, void *o,
+                      float *lse, float sm_scale, void *workspace, size_t workspace_bytes,
+                      void *stream)
 {
     if (p == nullptr || p->shared == nullptr)
         return fail(RP_EINVAL, "plan must come from rp_plan_create_shared_prefix");
@@ -552,8 +556,7 @@ int rp_run_shared_prefix(const rp_plan *p, const void *q, const void *k_shared,
     if (st != RP_OK)
         return st;
     // 2. each request against its own keys, into o
-    st = run_plan(p, q, k_unique, v_unique, o, lse_unique, sm_scale, ws, L.o_shared, stream,
-                  nullptr, true);
+    st = run_plan(p, q, k_own, v_own, o, lse_unique, sm_scale, ws, L.o_shared, stream, paged, true);
     if (st != RP_OK)
         return st;
     // 3. o, lse = merge(shared state, own state), in place over o
@@ -571,6 +574,28 @@ int rp_run_shared_prefix(const rp_plan *p, const void *q, const void *k_shared,
     a.head_dim = sh.head_dim;
     a.num_states = 2;
     return launch_merge(a, stream);
+}
+
+}  // namespace
+
+int rp_run_shared_prefix(const rp_plan *p, const void *q, const void *k_shared,
+                         const void *v_shared, const void *k_unique, const void *v_unique, void *o,
+                         float *lse, float sm_scale, void *workspace, size_t workspace_bytes,
+                         void *stream)
+{
+    return run_shared_prefix(p, q, k_shared, v_shared, k_unique, v_unique, nullptr, o, lse,
+                             sm_scale, workspace, workspace_bytes, stream);
+}
+
+int rp_run_shared_prefix_paged(const rp_plan *p, const void *q, const void *k_shared,
+                               const void *v_shared, const void *k_pages, const void *v_pages,
+                               const int32_t *block_table, int max_blocks_per_seq, int page_size,
+                               void *o, float *lse, float sm_scale, void *workspace,
+                               size_t workspace_bytes, void *stream)
+{
+    PagedKV pk{block_table, max_blocks_per_seq, page_size};
+    return run_shared_prefix(p, q, k_shared, v_shared, k_pages, v_pages, &pk, o, lse, sm_scale,
+                             workspace, workspace_bytes, stream);
 }
 
 int rp_merge_state(const void *v_a, const float *s_a, const void *v_b, const float *s_b,
