@@ -45,6 +45,9 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr float kLn2 = 0.693147180559945309f;
 // lazy-rescale threshold in log2 units
 constexpr float kRescaleLog2 = 8.0f;
+// a lane's part of a block's row sum at most this (2^(threshold - 1)) keeps
+// the reference max (fast path of the softmax update)
+constexpr float kFastSumMax = 128.0f;
 
 template <int HD>
 struct Tile {
@@ -189,69 +192,98 @@ __device__ __attribute__((always_inline)) inline void block_step(
     }
     __builtin_amdgcn_sched_barrier(0);
     // S^T register j of row block n holds key 32 n + 8 (j / 4) + 4 h + j % 4
-    float mx = -INFINITY;
-    if (POS_SCALE) {
+    float p[T::NB][16];
+    float t8[T::NB * 8];
+    // p = 2^(scaled score - m_use), and this lane's part of the row sum from
+    // the fp32 P (the LSE needs it exact) as a fixed pairwise tree
+    auto exp_sum = [&](float m_use) __attribute__((always_inline)) {
 #pragma unroll
         for (int n = 0; n < T::NB; ++n)
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                if (MASK && 32 * n + 8 * (j >> 2) + (j & 3) >= thr)
-                    s[n][j] = -INFINITY;
-                mx = fmaxf(mx, s[n][j]);
+                const float x = POS_SCALE ? __builtin_fmaf(s[n][j], c, -m_use) : s[n][j] - m_use;
+                p[n][j] = fast_exp2(x);
             }
-        mx = pair_max(mx) * c;
-    } else {
 #pragma unroll
         for (int n = 0; n < T::NB; ++n)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                float x = s[n][j] * c;
-                if (MASK && 32 * n + 8 * (j >> 2) + (j & 3) >= thr)
-                    x = -INFINITY;
-                s[n][j] = x;
-                mx = fmaxf(mx, x);
-            }
-        mx = pair_max(mx);
-    }
+            for (int j = 0; j < 8; ++j)
+                t8[n * 8 + j] = p[n][2 * j] + p[n][2 * j + 1];
+#pragma unroll
+        for (int w = T::NB * 4; w >= 1; w >>= 1)
+#pragma unroll
+            for (int j = 0; j < w; ++j)
+                t8[j] = t8[2 * j] + t8[2 * j + 1];
+    };
     // Lazy rescaling: the reference max only moves when the block max
     // exceeds it by more than 2^8 (p <= 256 stays exact enough in bf16 and
     // fp32); O, l and the LSE are all taken relative to the same reference,
     // so the result does not depend on when it moves.
-    const bool grow = mx > st.m + kRescaleLog2;
-    const float m_ref = grow ? mx : st.m;
-    const float m_use = m_ref == -INFINITY ? 0.0f : m_ref;
-    float p[T::NB][16];
+    //
+    // Fast path (positive scale): P is first computed against the current
+    // reference.  If every lane's part of the row sum is at most 2^7, every
+    // p is, so no score of the block exceeds the reference by 8 (with a
+    // margin of one binade for rounding) and the reference stays: those P
+    // are exactly the ones the full update computes, and the block max is
+    // never needed.  A reference still at -inf (no visible key yet) gives
+    // p = inf or NaN, which fails the test.  Otherwise the wave takes the
+    // full update below.  (At head_dim 256 the extra live registers of the
+    // fast path spill, so that kernel always takes the full update.)
+    constexpr bool FAST = POS_SCALE && HD == 128;
+    bool full = true;
+    if (FAST) {
+        if (MASK) {
 #pragma unroll
-    for (int n = 0; n < T::NB; ++n)
+            for (int n = 0; n < T::NB; ++n)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const float x = POS_SCALE ? __builtin_fmaf(s[n][j], c, -m_use) : s[n][j] - m_use;
-            p[n][j] = fast_exp2(x);
+                for (int j = 0; j < 16; ++j)
+                    if (32 * n + 8 * (j >> 2) + (j & 3) >= thr)
+                        s[n][j] = -INFINITY;
         }
-    // row-sum part of this lane, from the fp32 P (the LSE needs it exact):
-    // fixed pairwise tree
-    float t8[T::NB * 8];
+        exp_sum(st.m);
+        full = __any(!(t8[0] <= kFastSumMax));
+    }
+    if (full) {
+        float mx = -INFINITY;
+        if (POS_SCALE) {
 #pragma unroll
-    for (int n = 0; n < T::NB; ++n)
+            for (int n = 0; n < T::NB; ++n)
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            t8[n * 8 + j] = p[n][2 * j] + p[n][2 * j + 1];
+                for (int j = 0; j < 16; ++j) {
+                    if (!FAST && MASK && 32 * n + 8 * (j >> 2) + (j & 3) >= thr)
+                        s[n][j] = -INFINITY;
+                    mx = fmaxf(mx, s[n][j]);
+                }
+            mx = pair_max(mx) * c;
+        } else {
 #pragma unroll
-    for (int w = T::NB * 4; w >= 1; w >>= 1)
+            for (int n = 0; n < T::NB; ++n)
 #pragma unroll
-        for (int j = 0; j < w; ++j)
-            t8[j] = t8[2 * j] + t8[2 * j + 1];
-    if (__any(grow)) {
-        const float alpha = fast_exp2(st.m - m_use);   // 1 where the reference stays, 0 at the start
-        st.l *= alpha;
+                for (int j = 0; j < 16; ++j) {
+                    float x = s[n][j] * c;
+                    if (MASK && 32 * n + 8 * (j >> 2) + (j & 3) >= thr)
+                        x = -INFINITY;
+                    s[n][j] = x;
+                    mx = fmaxf(mx, x);
+                }
+            mx = pair_max(mx);
+        }
+        const bool grow = mx > st.m + kRescaleLog2;
+        const float m_ref = grow ? mx : st.m;
+        const float m_use = m_ref == -INFINITY ? 0.0f : m_ref;
+        exp_sum(m_use);
+        if (__any(grow)) {
+            const float alpha = fast_exp2(st.m - m_use);   // 1 where the reference stays, 0 at the start
+            st.l *= alpha;
 #pragma unroll
-        for (int db = 0; db < T::DB; ++db)
+            for (int db = 0; db < T::DB; ++db)
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-                st.acc[db][j] *= alpha;
+                for (int j = 0; j < 16; ++j)
+                    st.acc[db][j] *= alpha;
+        }
+        st.m = m_ref;
     }
     st.l += t8[0];
-    st.m = m_ref;
 
     // P as the B operand of O^T += V^T P^T: k-step t of row block n takes,
     // in lane half h, element e = key 32 n + 16 t + 4 h + 8 (e / 4) + e % 4,
