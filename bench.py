@@ -94,6 +94,9 @@ def parse_args():
     p.add_argument("--paged", type=int, default=0, metavar="PAGE_SIZE",
                    help="keep K/V in a paged cache of this page size (rp_run_paged on a prebuilt plan)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--sample-steps", type=int, default=100,
+                   help="steps timed one by one (HIP events per step) after the timed region, "
+                        "for the per-step median and std, warm and cold (0: skip)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--copy-probe-mib", type=int, default=0)
@@ -232,6 +235,39 @@ def warm_up(step, warmup) -> int:
         n += 10
         torch.cuda.synchronize()
     return n
+
+
+FLUSH_BYTES = 512 << 20   # larger than L2 (4 MB per XCD) and MALL (256 MB) together
+
+
+def per_step_times(step, stream, n: int, flops: float):
+    """Per-step GPU times (HIP events around each step on `stream`), after the
+    timed region: warm (back to back) and cold (a 512 MiB device write between
+    steps evicts L2 and MALL).  Median and standard deviation in ms, and the
+    median as TFLOP/s."""
+    import torch
+    if n <= 0:
+        return None
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=torch.device("cuda:0"))
+
+    def run(cold: bool):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for i, (a, b) in enumerate(evs):
+            if cold:
+                flush.fill_(i & 0xff)
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(b) for a, b in evs])
+        med = float(np.median(t))
+        return {"median_ms": med, "std_ms": float(np.std(t)), "median_tflops": flops / (med * 1e-3) / 1e12}
+
+    with torch.cuda.stream(stream):
+        res = {"n": n, "warm": run(False), "cold": run(True), "flush_bytes": FLUSH_BYTES}
+    del flush
+    return res
 
 
 def _time_steps(step, warmup, steps: int, stream):
@@ -501,6 +537,9 @@ def main():
     ms_per_step = wall_s * 1e3 / args.steps
     gpu_ms_per_step = event_ms / args.steps
 
+    per_step = per_step_times(lambda: _lib.check(step(*call_args), step_name), stream,
+                              args.sample_steps, flops)
+
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (gpu_ms_per_step * 1e-3) / 1e12
     kernel = f"tile_kernel_hd{cfg.head_dim}"
@@ -549,6 +588,7 @@ def main():
         "gpu_ms_per_step": gpu_ms_per_step,
         "launches_per_step": launches,
         "plan_ms_median": float(np.median(plan_times) * 1e3),
+        "per_step": per_step,
         "roofline": roofline,
         "cpu_baseline": None,
     }
