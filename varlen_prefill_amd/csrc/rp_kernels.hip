@@ -276,10 +276,26 @@ __device__ __attribute__((always_inline)) inline void block_step(
             const float alpha = fast_exp2(st.m - m_use);   // 1 where the reference stays, 0 at the start
             st.l *= alpha;
 #pragma unroll
-            for (int db = 0; db < T::DB; ++db)
+            for (int db = 0; db < T::DB; ++db) {
+                if constexpr (HD == 256) {
+                    // The accumulators live in AGPRs (the MFMAs read and
+                    // write them there).  Multiplied in place through one
+                    // VGPR at a time, so that the copies to and from VGPRs
+                    // stay in this rarely taken branch instead of being
+                    // hoisted to the top of every key-block iteration.
 #pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    st.acc[db][j] *= alpha;
+                    for (int j = 0; j < 16; ++j) {
+                        float t;
+                        asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(t) : "a"(st.acc[db][j]));
+                        t *= alpha;
+                        asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(st.acc[db][j]) : "v"(t));
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        st.acc[db][j] *= alpha;
+                }
+            }
         }
         st.m = m_ref;
     }
