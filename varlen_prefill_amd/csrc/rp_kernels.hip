@@ -227,9 +227,8 @@ __device__ __attribute__((always_inline)) inline void block_step(
     // are exactly the ones the full update computes, and the block max is
     // never needed.  A reference still at -inf (no visible key yet) gives
     // p = inf or NaN, which fails the test.  Otherwise the wave takes the
-    // full update below.  (At head_dim 256 the extra live registers of the
-    // fast path spill, so that kernel always takes the full update.)
-    constexpr bool FAST = POS_SCALE && HD == 128;
+    // full update below.
+    constexpr bool FAST = POS_SCALE;
     bool full = true;
     if (FAST) {
         if (MASK) {
