@@ -555,7 +555,7 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
         if (FP8)
             issue_fp8(kb);
         else
-            issue_loads(kb, HD == 128 ? kb % T::STAGES : kb - kb_begin);
+            issue_loads(kb, kb % T::STAGES);
     }
     if (PAGED && kb_pre < kb_end)
         page_id(kb_pre);
@@ -591,7 +591,7 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
 
     wait_loads(kb_pre - kb_begin - 1);
     if (FP8 && kb_begin < kb_end)
-        convert_fp8(HD == 128 ? kb_begin % T::STAGES : 0);
+        convert_fp8(kb_begin % T::STAGES);
     __syncthreads();
 
     // Blocks below the first row's causal limit need no mask; they come
@@ -608,32 +608,6 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
         constexpr bool MASK = decltype(mask_tag)::value;
         constexpr bool HILO = decltype(hilo_tag)::value;
         static_assert(T::STAGES == 2, "the loops assume two stages");
-        if constexpr (HD != 128) {
-            // head_dim 256: stage (kb - kb_begin) % STAGES, one block per iteration
-            for (int kb = kb_from; kb < kb_to; ++kb) {
-                const int buf = (kb - kb_begin) % T::STAGES;
-                const int kb_next = kb + T::STAGES - 1;
-                if (kb_next < kb_end) {
-                    if (FP8)
-                        issue_fp8(kb_next);
-                    else
-                        issue_loads(kb_next, (kb_next - kb_begin) % T::STAGES);
-                    if (PAGED && kb + T::STAGES < kb_end)
-                        page_id(kb + T::STAGES);
-                }
-                const char *Ks = smem + buf * T::STAGE_BYTES;
-                const char *Vs = Ks + T::TILE_BYTES;
-                const int thr = lim_row - kb * T::BK - 4 * h;
-                block_step<HD, POS_SCALE, MASK, HILO>(st, Ks, Vs, c, thr, qc, h, grp, s16);
-                wait_loads(min(kb_end, kb + T::STAGES) - (kb + 2));
-                // fp8: the staging slot holds one block, so two stages keep
-                // one block in flight, converted here
-                if (FP8 && kb_next < kb_end)
-                    convert_fp8((kb_next - kb_begin) % T::STAGES);
-                __syncthreads();
-            }
-            return;
-        }
         auto step = [&](int kb, auto buf_tag) __attribute__((always_inline)) {
             constexpr int BUF = decltype(buf_tag)::value;
             if (kb + 1 < kb_end) {
@@ -648,7 +622,7 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
             const char *Ks = smem + BUF * T::STAGE_BYTES;
             const char *Vs = Ks + T::TILE_BYTES;
             const int thr = lim_row - kb * T::BK - 4 * h;
-            if (wave_rows)
+            if (HD != 128 || wave_rows)
                 block_step<HD, POS_SCALE, MASK, HILO>(st, Ks, Vs, c, thr, qc, h, grp, s16);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // block kb + 1 has landed
             if (FP8 && kb + 1 < kb_end)
