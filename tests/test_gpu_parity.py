@@ -220,30 +220,45 @@ def test_graph_capture_replays():
     plan.close()
 
 
-@pytest.mark.parametrize("name", ["hd128_gqa_causal", "ragged64", "decode64", "decode_few", "mixed"])
-def test_full_size_config_sampled(name):
+# (workload, causal, edge tokens per request end, random rows); the append
+# workload's rows see up to 16K keys, so fewer of them are sampled
+FULL_SIZE = [
+    ("hd128_gqa_causal", True, 40, 3000),
+    ("ragged64", True, 40, 3000),
+    ("decode64", True, 40, 3000),
+    ("decode_few", True, 40, 3000),
+    ("mixed", True, 40, 3000),
+    ("hd256_gqa", True, 40, 3000),
+    ("hd256_gqa", False, 40, 3000),
+    ("append_prefix", True, 4, 2000),
+]
+
+
+@pytest.mark.parametrize("case", FULL_SIZE, ids=[f"{n}{'' if c else '_noncausal'}" for n, c, _, _ in FULL_SIZE])
+def test_full_size_config_sampled(case):
     """Full-size workloads in the benchmark's launch configuration: every head
-    of the first/last 40 tokens of each request and 3000 random rows are
-    checked against the oracle row by row."""
+    of the first/last `edge` tokens of each request and `nrand` random rows
+    are checked against the oracle row by row."""
+    name, causal, edge, nrand = case
     cfg = get_config(name)
     b = make_config_batch(cfg)
     sm = default_scale(cfg.head_dim)
-    o, lse = _gpu(b, cfg.causal, sm)
+    o, lse = _gpu(b, causal, sm)
     rng = np.random.default_rng(123)
     toks = []
     for r in range(b.batch):
         q0, q1 = int(b.q_indptr[r]), int(b.q_indptr[r + 1])
-        toks += list(range(q0, min(q1, q0 + 40))) + list(range(max(q0, q1 - 40), q1))
+        toks += list(range(q0, min(q1, q0 + edge))) + list(range(max(q0, q1 - edge), q1))
     toks = np.unique(np.array(toks, dtype=np.int64))
     tt = np.repeat(toks, cfg.num_qo_heads)
     hh = np.tile(np.arange(cfg.num_qo_heads), toks.size)
     total = int(b.q_indptr[-1])
-    rt = rng.integers(0, total, 3000)
-    rh = rng.integers(0, cfg.num_qo_heads, 3000)
+    rt = rng.integers(0, total, nrand)
+    rh = rng.integers(0, cfg.num_qo_heads, nrand)
     tt = np.concatenate([tt, rt])
     hh = np.concatenate([hh, rh])
     ro, rl = oracle.ragged_attention_rows(b.q, b.k, b.v, b.q_indptr, b.kv_indptr,
-                                          cfg.num_qo_heads, cfg.num_kv_heads, cfg.causal, sm,
+                                          cfg.num_qo_heads, cfg.num_kv_heads, causal, sm,
                                           tt, hh)
     og = bf16_to_f64(o)[tt, hh]
     lg = lse.double().numpy()[tt, hh]
