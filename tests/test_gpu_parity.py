@@ -220,16 +220,38 @@ def test_graph_capture_replays():
     plan.close()
 
 
+# Full-size workloads whose every row the oracle computes in seconds to tens of
+# seconds: (workload, causal)
+FULL_ROWS = [
+    ("hd128_gqa_causal", True),
+    ("ragged64", True),
+    ("hd256_gqa", True),
+    ("hd256_gqa", False),
+]
+
+
+@pytest.mark.parametrize("case", FULL_ROWS, ids=[f"{n}{'' if c else '_noncausal'}" for n, c in FULL_ROWS])
+def test_full_size_config_all_rows(case):
+    """Full-size workloads in the benchmark's launch configuration (one-shot
+    plan with default chunking), every (token, qo head) row against the
+    oracle."""
+    name, causal = case
+    cfg = get_config(name)
+    b = make_config_batch(cfg)
+    sm = default_scale(cfg.head_dim)
+    o, lse = _gpu(b, causal, sm)
+    ro, rl = _oracle(b, causal, sm)
+    rep = compare(bf16_to_f64(o), lse.double().numpy(), ro, rl)
+    print(f"{name} causal={causal}: {rep}")
+
+
 # (workload, causal, edge tokens per request end, random rows); the append
-# workload's rows see up to 16K keys, so fewer of them are sampled
+# workload's rows see up to 16K keys and the decode workloads up to 32K, so
+# their rows are sampled
 FULL_SIZE = [
-    ("hd128_gqa_causal", True, 40, 3000),
-    ("ragged64", True, 40, 3000),
     ("decode64", True, 40, 3000),
     ("decode_few", True, 40, 3000),
     ("mixed", True, 40, 3000),
-    ("hd256_gqa", True, 40, 3000),
-    ("hd256_gqa", False, 40, 3000),
     ("append_prefix", True, 4, 2000),
 ]
 
@@ -276,50 +298,11 @@ def _scale_keys(batch, factor):
             batch.k[k0:k1] = (batch.k[k0:k1].float() * f[:, None, None]).to(torch.bfloat16)
 
 
-def _check_bf16_p_bound(batch, causal, sm_scale, **plan_kw):
-    """GPU against the oracle with the error bound of the arithmetic itself,
-    for inputs whose softmax is dominated by a few keys in rows far past the
-    first 128 (there P enters the PV product rounded to bf16, and a few
-    dominant terms do not average its rounding out, so the fixed 8e-3 gate of
-    the N(0,1) workloads does not apply).  Per output element:
-      |O_gpu - O_ref| <= 2^-8 max_j |V_j| + 2^-8 |O_ref| + 1e-5,
-    the first term from rounding each p to bf16 (8 significant bits: relative
-    error <= 2^-8, the weights p_j / l summing to 1), the second from
-    rounding O to bf16 (half a bf16 ulp is at most 2^-8 |O|), the last for
-    the fp32 arithmetic; max_j runs over the request's keys of that kv head
-    and d.  Mean |err| and the
-    LSE keep their 1e-3 gates; fully masked rows stay exact."""
-    o, lse = _gpu(batch, causal, sm_scale, **plan_kw)
-    ro, rl = _oracle(batch, causal, sm_scale)
-    og = bf16_to_f64(o)
-    lg = lse.double().numpy()
-    g = batch.num_qo_heads // batch.num_kv_heads
-    vabs = batch.v.float().abs().numpy().astype(np.float64)
-    worst = 0.0
-    for r in range(batch.batch):
-        q0, q1 = int(batch.q_indptr[r]), int(batch.q_indptr[r + 1])
-        k0, k1 = int(batch.kv_indptr[r]), int(batch.kv_indptr[r + 1])
-        if q1 == q0:
-            continue
-        vmax = vabs[k0:k1].max(axis=0) if k1 > k0 else np.zeros(vabs.shape[1:])   # [Hkv, D]
-        vmax_q = np.repeat(vmax, g, axis=0)[None]                                  # [1, Hq, D]
-        masked = np.isneginf(rl[q0:q1])
-        assert np.array_equal(np.isneginf(lg[q0:q1]), masked)
-        assert np.all(og[q0:q1][masked] == 0.0)
-        live = ~masked
-        err = np.abs(og[q0:q1] - ro[q0:q1])
-        bound = 2.0 ** -8 * vmax_q + 2.0 ** -8 * np.abs(ro[q0:q1]) + 1e-5
-        assert np.all(err[live] <= bound[live]), (
-            f"request {r}: error {err[live].max():.3e} over the bf16-P bound")
-        worst = max(worst, float((err[live] / bound[live]).max()) if live.any() else 0.0)
-        assert np.all(np.abs(lg[q0:q1][live] - rl[q0:q1][live]) <= 1e-3)
-    rows = _rows_in_requests(batch)
-    live_rows = rows & ~np.isneginf(rl).all(axis=1)
-    assert np.abs(og[live_rows] - ro[live_rows]).mean() <= 1e-3
-    print(f"worst error / bound = {worst:.3f}")
+STRESS = ["growing", "sink", "wide_scale", "growing_split", "growing_hd256", "sink_hd256",
+          "wide_scale_hd256", "wide_scale_split"]
 
 
-@pytest.mark.parametrize("mode", ["growing", "sink", "wide_scale", "growing_split", "growing_hd256"])
+@pytest.mark.parametrize("mode", STRESS)
 def test_reference_max_moves(mode):
     """Score profiles that move the running reference max of the online
     softmax often and by large steps (keys that grow along the sequence, a
@@ -327,18 +310,19 @@ def test_reference_max_moves(mode):
     inputs almost never move it after a tile's first key block, so these
     cases drive the update paths that keep or move the reference (and the
     rescale of the accumulator) that the other tests rarely reach.  Their
-    softmax is dominated by few keys, so the check is the bf16-P error bound
-    (_check_bf16_p_bound)."""
-    d = 256 if mode == "growing_hd256" else 128
+    softmax is dominated by a few keys anywhere in a row, which is what the
+    kernel's split of P into bf16 hi + lo parts is for: they are held to the
+    same gates as every other case."""
+    d = 256 if mode.endswith("_hd256") else 128
     b = make_batch([200, 64, 700, 33], [200, 64, 700, 900], 8, 2, d, seed=3100)
     sm = default_scale(d)
     plan_kw = {}
     if mode.startswith("growing"):
         _scale_keys(b, lambda j: 1.0 + j / 48.0)
-    elif mode == "sink":
+    elif mode.startswith("sink"):
         _scale_keys(b, lambda j: torch.where(j == 0, 6.0, 1.0))
-    elif mode == "wide_scale":
+    elif mode.startswith("wide_scale"):
         sm = 1.0
-    if mode == "growing_split":
+    if mode.endswith("_split"):
         plan_kw["kv_chunk"] = 128
-    _check_bf16_p_bound(b, True, sm, **plan_kw)
+    _check_full(b, True, sm, **plan_kw)

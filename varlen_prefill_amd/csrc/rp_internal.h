@@ -32,10 +32,31 @@ constexpr int kChunkAlign = 64;     // kv_chunk must be a multiple of this
 constexpr int kDecodeRows = 32;
 constexpr int kDecodeChunk = 2048;
 constexpr int kDefaultXcds = 8;     // MI355X: 8 XCDs, workgroups dispatched round-robin
-// Key blocks are computed with P split into a bf16 hi part and a bf16 lo
-// remainder when the tile's first row sees at most this many keys (and, at
-// head_dim 256, on blocks partially masked for the tile).
+// P enters the PV product either rounded to bf16 or split into a bf16 hi part
+// and a bf16 lo remainder (two MFMAs, accurate to about 2^-17).
+//
+// Tiles whose first row sees at most kHiLoKeys keys split P on every block:
+// their rows see few keys, so single keys carry much of the softmax.
+//
+// Other tiles of final (unsplit) items round P to bf16; an item whose result
+// holds an output element with |O| >= kRecomputeAbsO is computed again with P
+// split on every block.  From 2 up, half a bf16 ulp of O (7.8e-3 in [2, 4))
+// leaves almost none of the 8e-3 max-abs gate to the rest of the arithmetic;
+// below kRecomputeAbsO it leaves at least 4.1e-3, which the 2^-9 relative
+// rounding of the softmax weights reaches only where the weighted mean of
+// |V| exceeds 2.1 while |O| stays below 1.5 (large values of both signs
+// cancelling under a few dominant keys).
+//
+// Partial states of split-KV tiles cannot be recomputed after the merge, so
+// they split P in the key blocks where some row of the wave has a key whose p
+// exceeds kHiLoFracPartial of the row's running sum (the block included):
+// every key left rounded ends with a weight of at most that fraction.
 constexpr int kHiLoKeys = 128;
+#ifndef RP_RECOMPUTE_ABS_O
+#define RP_RECOMPUTE_ABS_O 1.5f
+#endif
+constexpr float kRecomputeAbsO = RP_RECOMPUTE_ABS_O;
+constexpr float kHiLoFracPartial = 0.125f;
 
 // Key-block shape of the tile kernel: keys per block and LDS pipeline depth
 // (stages in flight, K and V of one block per stage).

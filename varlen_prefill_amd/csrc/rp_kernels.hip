@@ -14,11 +14,19 @@
 // with transposed products keeps every row's scores inside one lane pair and
 // lets P feed the second MFMA straight from registers.
 //
-// P is rounded to bf16 for the PV MFMA.  In tiles whose first row sees at
-// most kHiLoKeys keys (and, at head_dim 256, on partially masked blocks),
-// P is split into bf16 hi + bf16 lo (two MFMAs), which keeps rows with few
-// keys accurate to well under one bf16 ulp of O; rows that see more keys
-// average the rounding of P over many terms.
+// P enters the PV MFMA either rounded to bf16 or split into bf16 hi + bf16
+// lo parts (two MFMAs, accurate to about 2^-17), which keeps output elements
+// within the error gate where single keys carry much of a row's softmax:
+//  * tiles whose rows see few keys split P on every block;
+//  * other final items round P, and a workgroup whose result holds an
+//    element with |O| >= kRecomputeAbsO (where the output's own bf16
+//    rounding leaves little of the gate) computes the item again with P
+//    split on every block;
+//  * partial states of split-KV tiles (merged later, so not recomputable)
+//    split P in the key blocks where some row of the wave has a key whose p
+//    exceeds kHiLoFracPartial of the row's running sum.
+// Every decision reads only the tile's own scores and outputs, so results
+// stay independent of the batch.
 //
 // merge_kernel: folds the fp32 partial states of split tiles, chunk by chunk
 // in ascending key order (merge of attention states, page
@@ -129,13 +137,14 @@ struct WaveState {
 // One key block of one wave: S^T = K Q^T, mask, online softmax update,
 // O^T += V^T P^T.  MASK: the block holds keys beyond some row's causal limit
 // (the diagonal or the KV tail); thr is this lane's visible-key bound
-// relative to the block start and lane half.  HILO: P enters the PV product
-// as a bf16 hi part plus a bf16 lo remainder.  Each variant is straight-line
-// code so that LDS reads, MFMAs and VALU work can be interleaved.
-template <int HD, bool POS_SCALE, bool MASK, bool HILO>
+// relative to the block start and lane half; valid: this lane's row is a
+// row of the tile.  FORCE and trig choose how P enters the PV product (see
+// below).  Each variant is straight-line code so that LDS reads, MFMAs and
+// VALU work can be interleaved.
+template <int HD, bool POS_SCALE, bool MASK, bool FORCE>
 __device__ __attribute__((always_inline)) inline void block_step(
-    WaveState<HD> &st, const char *Ks, const char *Vs, float c, int thr, int qc, int h,
-    int grp, int s16)
+    WaveState<HD> &st, const char *Ks, const char *Vs, float c, int thr, bool valid, bool trig,
+    float kappa, int qc, int h, int grp, int s16)
 {
     using T = Tile<HD>;
     f32x16 s[T::NB];
@@ -228,8 +237,22 @@ __device__ __attribute__((always_inline)) inline void block_step(
     // never needed.  A reference still at -inf (no visible key yet) gives
     // p = inf or NaN, which fails the test.  Otherwise the wave takes the
     // full update below.
+    //
+    // FORCE: P enters the PV product split into bf16 hi + lo parts on every
+    // block.  Otherwise, with trig (partial states of split-KV tiles), it is
+    // split in blocks where some valid row of the wave has a key with
+    // p > kHiLoFracPartial * (the row's running sum, this block included),
+    // and rounded to bf16 elsewhere; without trig it is rounded to bf16 (the
+    // caller recomputes the item where that matters).  A lane whose block
+    // sum t is at most the fraction of its own running sum l + t holds no
+    // such p (its sum is part of its row's): the fast path tests
+    // t <= kappa l in every valid lane next to its own test (kappa = frac /
+    // (1 - frac), infinite without trig), and only waves that fail it look
+    // at the block's largest p.  Both tests come from the same values, so
+    // the second branch does not wait for the VALU.
     constexpr bool FAST = POS_SCALE;
     bool full = true;
+    bool check = !FORCE && trig;
     if (FAST) {
         if (MASK) {
 #pragma unroll
@@ -239,10 +262,13 @@ __device__ __attribute__((always_inline)) inline void block_step(
                     if (32 * n + 8 * (j >> 2) + (j & 3) >= thr)
                         s[n][j] = -INFINITY;
         }
+        const float lim_t = valid ? kappa * st.l : INFINITY;
         exp_sum(st.m);
         full = __any(!(t8[0] <= kFastSumMax));
+        if (!FORCE)
+            check = __any(t8[0] > lim_t);
     }
-    if (full) {
+    if (__builtin_expect(full, !FAST)) {
         float mx = -INFINITY;
         if (POS_SCALE) {
 #pragma unroll
@@ -297,38 +323,57 @@ __device__ __attribute__((always_inline)) inline void block_step(
             }
         }
         st.m = m_ref;
+        check = !FORCE && trig;
     }
     st.l += t8[0];
+    bool split = FORCE;
+    if (!FORCE && __builtin_expect(check, !FAST)) {
+        float pm = 0.0f;
+#pragma unroll
+        for (int n = 0; n < T::NB; ++n)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                pm = fmaxf(pm, p[n][j]);
+        split = __any(valid && pm > kHiLoFracPartial * pair_sum(st.l));
+    }
 
     // P as the B operand of O^T += V^T P^T: k-step t of row block n takes,
     // in lane half h, element e = key 32 n + 16 t + 4 h + 8 (e / 4) + e % 4,
     // i.e. this lane's S^T registers j = 8 t + e.
     bf16x8 ph[T::NB][2];
-    bf16x8 pl[T::NB][2];
 #pragma unroll
     for (int n = 0; n < T::NB; ++n)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float pv = p[n][8 * t + e];
-                const __bf16 hb = (__bf16)pv;
-                ph[n][t][e] = hb;
-                if (HILO)
-                    pl[n][t][e] = (__bf16)(pv - (float)hb);
-            }
-
+            for (int e = 0; e < 8; ++e)
+                ph[n][t][e] = (__bf16)p[n][8 * t + e];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int db = 0; db < T::DB; ++db)
 #pragma unroll
         for (int n = 0; n < T::NB; ++n)
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
+            for (int t = 0; t < 2; ++t)
                 st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db][n][t], ph[n][t], st.acc[db], 0, 0, 0);
-                if (HILO)
+    if (__builtin_expect(split, 0)) {
+        // the lo parts bf16(p - bf16(p))
+        bf16x8 pl[T::NB][2];
+#pragma unroll
+        for (int n = 0; n < T::NB; ++n)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    pl[n][t][e] = (__bf16)(p[n][8 * t + e] - (float)ph[n][t][e]);
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+            for (int n = 0; n < T::NB; ++n)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
                     st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db][n][t], pl[n][t], st.acc[db], 0, 0, 0);
-            }
+    }
 }
 
 template <int HD, bool POS_SCALE, bool PAGED, bool FP8>
@@ -360,7 +405,6 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
     const float c = a.scale_log2;
     const int kb_begin = it.key_begin / T::BK;
     const int kb_end = it.key_end > it.key_begin ? (it.key_end + T::BK - 1) / T::BK : kb_begin;
-    const bool hilo_all = it.lim_first <= kHiLoKeys;
 
     const size_t head_off = ((size_t)(PAGED ? 0 : it.kv_row0) * a.num_kv_heads + it.kv_head) * HD;
     const __bf16 *kbase = static_cast<const __bf16 *>(a.k) + head_off;
@@ -549,16 +593,19 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
     // parity, so that the unrolled loop below knows every stage at compile
     // time and LDS addresses become per-lane constants plus an immediate).
     const int kb_pre = min(kb_begin + T::STAGES - 1, kb_end);
-    for (int kb = kb_begin; kb < kb_pre; ++kb) {
-        if (PAGED)
-            page_id(kb);
-        if (FP8)
-            issue_fp8(kb);
-        else
-            issue_loads(kb, kb % T::STAGES);
-    }
-    if (PAGED && kb_pre < kb_end)
-        page_id(kb_pre);
+    auto first_loads = [&]() __attribute__((always_inline)) {
+        for (int kb = kb_begin; kb < kb_pre; ++kb) {
+            if (PAGED)
+                page_id(kb);
+            if (FP8)
+                issue_fp8(kb);
+            else
+                issue_loads(kb, kb % T::STAGES);
+        }
+        if (PAGED && kb_pre < kb_end)
+            page_id(kb_pre);
+    };
+    first_loads();
 
     WaveState<HD> st;
     {
@@ -581,18 +628,20 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
 #pragma unroll
     for (int ds = 0; ds < T::DS; ++ds)
         asm volatile("" :: "v"(st.qf[ds]));
+    auto start = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int db = 0; db < T::DB; ++db)
+        for (int db = 0; db < T::DB; ++db)
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-            st.acc[db][j] = 0.0f;
-    st.m = -INFINITY;
-    st.l = 0.0f;
-
-    wait_loads(kb_pre - kb_begin - 1);
-    if (FP8 && kb_begin < kb_end)
-        convert_fp8(kb_begin % T::STAGES);
-    __syncthreads();
+            for (int j = 0; j < 16; ++j)
+                st.acc[db][j] = 0.0f;
+        st.m = -INFINITY;
+        st.l = 0.0f;
+        wait_loads(kb_pre - kb_begin - 1);
+        if (FP8 && kb_begin < kb_end)
+            convert_fp8(kb_begin % T::STAGES);
+        __syncthreads();
+    };
+    start();
 
     // Blocks below the first row's causal limit need no mask; they come
     // first.  The rest (diagonal and KV tail) are masked.  Each range runs as
@@ -604,9 +653,19 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
     // other workgroup on the CU (FP8 decode 14 % faster).  Uniform per wave.
     // (At head_dim 256, one workgroup per CU, the branch only costs spills.)
     const bool wave_rows = w * 32 < it.n_tok * g;
-    auto run = [&](auto mask_tag, auto hilo_tag, int kb_from, int kb_to) __attribute__((always_inline)) {
+    // Tiles whose first row sees at most kHiLoKeys keys (rows with few keys,
+    // where single keys carry much of the softmax) split P on every block.
+    // Other final items round P to bf16 and are recomputed with P split on
+    // every block when the result holds an element with |O| >=
+    // kRecomputeAbsO (below); partial states of split-KV tiles cannot be
+    // recomputed later, so they split P per block by the running-sum test.
+    const bool final_item = it.slot < 0;
+    const bool force = it.lim_first <= kHiLoKeys;
+    const bool trig = !final_item;
+    const float kappa = trig ? kHiLoFracPartial / (1.0f - kHiLoFracPartial) : INFINITY;
+    auto run = [&](auto mask_tag, auto force_tag, int kb_from, int kb_to) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
-        constexpr bool HILO = decltype(hilo_tag)::value;
+        constexpr bool FORCE = decltype(force_tag)::value;
         static_assert(T::STAGES == 2, "the loops assume two stages");
         auto step = [&](int kb, auto buf_tag) __attribute__((always_inline)) {
             constexpr int BUF = decltype(buf_tag)::value;
@@ -623,7 +682,8 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
             const char *Vs = Ks + T::TILE_BYTES;
             const int thr = lim_row - kb * T::BK - 4 * h;
             if (HD != 128 || wave_rows)
-                block_step<HD, POS_SCALE, MASK, HILO>(st, Ks, Vs, c, thr, qc, h, grp, s16);
+                block_step<HD, POS_SCALE, MASK, FORCE>(st, Ks, Vs, c, thr, row_valid, trig, kappa,
+                                                       qc, h, grp, s16);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // block kb + 1 has landed
             if (FP8 && kb + 1 < kb_end)
                 convert_fp8(BUF ^ 1);
@@ -641,22 +701,46 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
         if (kb < kb_to)
             step(kb, std::integral_constant<int, 0>{});
     };
-    if constexpr (HD == 128) {
-        if (hilo_all) {
-            run(std::false_type{}, std::true_type{}, kb_begin, kb_mask);
-            run(std::true_type{}, std::true_type{}, kb_mask, kb_end);
-        } else {
-            run(std::false_type{}, std::false_type{}, kb_begin, kb_mask);
-            run(std::true_type{}, std::false_type{}, kb_mask, kb_end);
-        }
-    } else {
-        // head_dim 256 keeps hi/lo on every masked block: one loop variant
-        // less keeps its register allocation free of spills in the loops
-        if (hilo_all)
-            run(std::false_type{}, std::true_type{}, kb_begin, kb_mask);
-        else
-            run(std::false_type{}, std::false_type{}, kb_begin, kb_mask);
+    auto run_forced = [&]() __attribute__((always_inline)) {
+        run(std::false_type{}, std::true_type{}, kb_begin, kb_mask);
         run(std::true_type{}, std::true_type{}, kb_mask, kb_end);
+    };
+    if (force) {
+        run_forced();
+    } else {
+        run(std::false_type{}, std::false_type{}, kb_begin, kb_mask);
+        run(std::true_type{}, std::false_type{}, kb_mask, kb_end);
+        if (final_item) {
+            // Recompute?  A wave votes for it when one of its valid rows has
+            // an output element with |O| >= kRecomputeAbsO; the flags of the
+            // four waves are combined through LDS (after the staging area,
+            // which the epilogue reuses), and the workgroup recomputes
+            // together (the K/V staging is shared).
+            bool redo = false;
+            {
+                const float lt = pair_sum(st.l);
+                float omax = 0.0f;
+#pragma unroll
+                for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        omax = fmaxf(omax, fabsf(st.acc[db][j]));
+                if (FP8)
+                    omax *= fabsf(a.v_scale);
+                redo = row_valid && lt > 0.0f && omax >= kRecomputeAbsO * lt;
+            }
+            int *flags = reinterpret_cast<int *>(smem + Tile<HD>::LDS_BYTES + (FP8 ? 2 * T::BK * HD : 0));
+            const bool wave_redo = __any(redo);
+            if (lane == 0)
+                flags[w] = wave_redo ? 1 : 0;
+            __syncthreads();
+            const int4 f = *reinterpret_cast<const int4 *>(flags);
+            if (f.x | f.y | f.z | f.w) {
+                first_loads();
+                start();
+                run_forced();
+            }
+        }
     }
 
     // ---- epilogue ----
@@ -753,9 +837,10 @@ __global__ __launch_bounds__(kThreads, HD == 128 ? 2 : 1) void tile_kernel(TileA
         tile_body<HD, false, PAGED, FP8>(a, it, smem);
 }
 
-// dynamic LDS of a tile kernel instance: the K/V stages, plus the fp8 staging slots
+// dynamic LDS of a tile kernel instance: the K/V stages, the fp8 staging
+// slots, and the four per-wave recompute flags
 template <int HD, bool FP8>
-constexpr int tile_lds_bytes() { return Tile<HD>::LDS_BYTES + (FP8 ? 2 * Tile<HD>::BK * HD : 0); }
+constexpr int tile_lds_bytes() { return Tile<HD>::LDS_BYTES + (FP8 ? 2 * Tile<HD>::BK * HD : 0) + 16; }
 
 template <int HD>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a)

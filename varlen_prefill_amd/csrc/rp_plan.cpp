@@ -256,18 +256,15 @@ int build_plan(const int32_t *q_indptr, const int32_t *kv_indptr, const PlanShap
         return kEUnsupported;
     }
 
-    // cost: two MFMA halves per key block, one more on hi/lo blocks, plus a
-    // fixed epilogue share
+    // cost: two MFMA halves per key block, one more where the kernel is
+    // expected to split P (tiles whose rows see few keys), plus a fixed
+    // epilogue share
     for (Item &it : plan.items) {
         int64_t cost = 4;
         if (it.key_end > it.key_begin) {
             const int64_t kb0 = it.key_begin / bk;
             const int64_t kb1 = (it.key_end + bk - 1) / bk;
-            for (int64_t kb = kb0; kb < kb1; ++kb) {
-                const bool mask = (kb + 1) * bk > it.lim_first;
-                const bool hilo = it.lim_first <= kHiLoKeys || (mask && shape.head_dim == 256);
-                cost += hilo ? 3 : 2;
-            }
+            cost += (kb1 - kb0) * (it.lim_first <= kHiLoKeys ? 3 : 2);
         }
         it.cost = (int32_t)std::min<int64_t>(cost, INT32_MAX);
     }
