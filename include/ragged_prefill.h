@@ -48,8 +48,8 @@
  * device-resident worklist; destroy it only after the stream work that uses it
  * has completed.  The workspace of the two-phase API is caller-provided (the
  * "instance-owned workspace" of page "vllm-rlt PR #112", design notes and
- * review); the one-shot call grows a per-device workspace of its own on first
- * use and keeps it until the process ends.
+ * review); the one-shot call keeps workspaces of its own, one per (device,
+ * stream), grown on first use and kept until the process ends.
  */
 #ifndef RAGGED_PREFILL_H
 #define RAGGED_PREFILL_H
@@ -89,10 +89,24 @@ int rp_available(void);
  * One-shot call: plans and runs on `stream` (the ragged_prefill_bf16_hd128 /
  * _hd256 FFI of page "Module flashinfer", with head_dim an argument).
  * head_dim must be 128 or 256; num_qo_heads % num_kv_heads == 0;
- * sm_scale finite.  Plans are cached per (offsets, shape); the device
- * worklist upload of a new plan and the growth of the library-owned
- * workspace synchronise with the device once.  Not safe to call from several
- * host threads at once on one device: use the two-phase API for that.
+ * sm_scale finite.  Plans are cached per (device, offsets, shape), at most 8
+ * per device; the split-KV workspace is library-owned, one per (device,
+ * stream), at most 8 streams per device.
+ *
+ * Streams: calls enqueued on different streams use different workspaces, so
+ * they may run concurrently; calls on one stream are ordered by it.  The
+ * upload of a new plan's worklist is synchronous; growing a stream's
+ * workspace waits for that stream; evicting a cached plan or a stream's
+ * workspace waits for the device.  Calls from several host threads are
+ * serialised by the library.
+ *
+ * HIP graph capture: a call on a capturing stream must find its plan cached
+ * and its stream's workspace large enough (an earlier call with the same
+ * offsets on that stream ensures both); otherwise it returns RP_EINVAL and
+ * enqueues nothing.  A captured graph keeps using that plan and workspace:
+ * later one-shot calls that would evict them (more than 8 distinct plans or
+ * streams on the device) must not run while the graph may still be
+ * replayed.  The two-phase API has none of these limits.
  */
 int ragged_prefill_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
                         const int32_t *q_indptr, const int32_t *kv_indptr, int batch,
@@ -107,9 +121,8 @@ typedef struct rp_plan rp_plan;
 
 enum rp_split_mode {
     RP_SPLIT_AUTO = 0,    /* split every tile whose visible keys span more than one KV chunk */
-    RP_SPLIT_NEVER = 1,   /* one workgroup per tile, folding KV chunks in order
-                             (not implemented: rp_plan_create returns RP_EUNSUPPORTED) */
     RP_SPLIT_ALWAYS = 2   /* one workgroup per (tile, KV chunk) + merge kernel */
+    /* 1 is reserved (rp_plan_create returns RP_EINVAL for it) */
 };
 
 /* Planner options.  All-zero means defaults.  The KV chunk size fixes the

@@ -70,6 +70,7 @@ def _plan(qi, ki, hq=8, hkv=2, d=128, causal=True, **kw):
     (dict(hq=256, hkv=1), _lib.RP_EUNSUPPORTED),      # group above 128
     (dict(kv_chunk=100), _lib.RP_EINVAL),             # chunk not a multiple of 64
     (dict(split_mode=7), _lib.RP_EINVAL),
+    (dict(split_mode=1), _lib.RP_EINVAL),
 ])
 def test_plan_validation(kwargs, status):
     with pytest.raises(vp.RaggedPrefillError) as ei:

@@ -104,20 +104,49 @@ def test_split_kv_chunks(d):
         _check_full(b, causal, default_scale(d), kv_chunk=128)
 
 
-def test_batch_composition_bitwise():
+def _run_variant(batch, variant, **plan_kw):
+    """One batch through a fresh plan with contiguous bf16 K/V ("bf16"),
+    FP8 (E4M3) K/V ("fp8") or a paged bf16 cache of 16-key pages ("paged")."""
+    import varlen_prefill_amd as vp
+    from workloads import make_fp8_kv, make_paged
+    q = batch.q.to(DEV)
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((q.shape[0], batch.num_qo_heads), float("nan"), dtype=torch.float32, device=DEV)
+    plan = vp.Plan(batch.q_indptr, batch.kv_indptr, batch.num_qo_heads, batch.num_kv_heads,
+                   batch.head_dim, True, **plan_kw)
+    sm = default_scale(batch.head_dim)
+    if variant == "bf16":
+        plan.run(q, batch.k.to(DEV), batch.v.to(DEV), out=out, lse=lse, sm_scale=sm)
+    elif variant == "fp8":
+        k8, v8 = make_fp8_kv(batch, 0.5, 0.75)
+        plan.run_fp8kv(q, k8.to(DEV), v8.to(DEV), 0.5, 0.75, out=out, lse=lse, sm_scale=sm)
+    else:
+        pg = make_paged(batch, 16, seed=batch.seed + len(batch.qo_lens))
+        plan.run_paged(q, pg.k_pages.to(DEV), pg.v_pages.to(DEV),
+                       torch.from_numpy(pg.block_table).to(DEV), out=out, lse=lse, sm_scale=sm)
+    torch.cuda.synchronize()
+    plan.close()
+    return out.cpu(), lse.cpu()
+
+
+@pytest.mark.parametrize("d,variant", [(128, "bf16"), (256, "bf16"), (128, "fp8"), (256, "fp8"),
+                                       (128, "paged"), (256, "paged")])
+def test_batch_composition_bitwise(d, variant):
+    """Each request's bits do not depend on the batch: the request alone, in
+    the batch and in a permuted batch, with and without split KV, for every
+    kernel instance (head_dim 128 / 256; bf16, FP8 and paged K/V)."""
     lens_q = [130, 0, 1, 257, 64, 600]
     lens_kv = [130, 7, 1, 400, 64, 600]
-    sm = default_scale(128)
     for kv_chunk in (0, 192):
-        full = make_batch(lens_q, lens_kv, 8, 2, 128, seed=77)
-        fo, fl = _gpu(full, True, sm, kv_chunk=kv_chunk)
+        full = make_batch(lens_q, lens_kv, 8, 2, d, seed=77)
+        fo, fl = _run_variant(full, variant, kv_chunk=kv_chunk)
         perm = [5, 3, 0, 2, 4, 1]
-        pb = make_batch([lens_q[i] for i in perm], [lens_kv[i] for i in perm], 8, 2, 128, seed=77,
+        pb = make_batch([lens_q[i] for i in perm], [lens_kv[i] for i in perm], 8, 2, d, seed=77,
                         request_ids=perm)
-        po, pl = _gpu(pb, True, sm, kv_chunk=kv_chunk)
+        po, pl = _run_variant(pb, variant, kv_chunk=kv_chunk)
         for r in range(len(lens_q)):
-            alone = make_batch([lens_q[r]], [lens_kv[r]], 8, 2, 128, seed=77, request_ids=[r])
-            ao, al = _gpu(alone, True, sm, kv_chunk=kv_chunk)
+            alone = make_batch([lens_q[r]], [lens_kv[r]], 8, 2, d, seed=77, request_ids=[r])
+            ao, al = _run_variant(alone, variant, kv_chunk=kv_chunk)
             q0, q1 = int(full.q_indptr[r]), int(full.q_indptr[r + 1])
             pos = perm.index(r)
             p0, p1 = int(pb.q_indptr[pos]), int(pb.q_indptr[pos + 1])
@@ -189,6 +218,70 @@ def test_one_shot_entry_point_and_streams():
     e = torch.empty(0, 4, 128, dtype=torch.bfloat16, device=DEV)
     ek = torch.empty(0, 2, 128, dtype=torch.bfloat16, device=DEV)
     vp.ragged_prefill(e, ek, ek, [0], [0])
+
+
+def test_one_shot_two_streams_split_bitwise():
+    """Two one-shot calls whose plans split KV (decode-like requests, 2048-key
+    chunks), enqueued back to back on two streams with no synchronisation in
+    between, give the bits of the two-phase API: each stream has its own
+    partial-state workspace."""
+    import varlen_prefill_amd as vp
+    b1 = make_batch([1, 1, 3], [5000, 3000, 4500], 8, 2, 128, seed=41)
+    b2 = make_batch([1, 2], [6100, 2500], 8, 2, 128, seed=42)
+    refs = [_gpu(b, True, default_scale(128), fill=0.0) for b in (b1, b2)]
+    dev = [(b.q.to(DEV), b.k.to(DEV), b.v.to(DEV)) for b in (b1, b2)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s_ in streams:
+        s_.wait_stream(torch.cuda.current_stream())
+    results = []
+    for _ in range(4):
+        for i, (b, (q, k, v)) in enumerate(zip((b1, b2), dev)):
+            with torch.cuda.stream(streams[i]):
+                results.append((i, vp.ragged_prefill(q, k, v, b.q_indptr, b.kv_indptr, causal=True)))
+    torch.cuda.synchronize()
+    for i, (o, lse) in results:
+        ro, rl = refs[i]
+        assert torch.equal(o.cpu().view(torch.int16), ro.view(torch.int16))
+        assert torch.equal(lse.cpu().view(torch.int32), rl.view(torch.int32))
+
+
+def test_one_shot_graph_capture():
+    """A one-shot call captured into a HIP graph after a warm-up call on the
+    capturing stream replays to the eager bits; under capture, offsets with
+    no cached plan are refused before anything is enqueued."""
+    import varlen_prefill_amd as vp
+    b = make_batch([1, 2], [6100, 2500], 8, 2, 128, seed=43)
+    q, k, v = b.q.to(DEV), b.k.to(DEV), b.v.to(DEV)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[0], 8, dtype=torch.float32, device=DEV)
+    s_ = torch.cuda.Stream()
+    s_.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s_):
+        vp.ragged_prefill(q, k, v, b.q_indptr, b.kv_indptr, causal=True, out=out, lse=lse)
+    s_.synchronize()
+    ref_o, ref_l = out.clone(), lse.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s_):
+        vp.ragged_prefill(q, k, v, b.q_indptr, b.kv_indptr, causal=True, out=out, lse=lse)
+    for _ in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_o.view(torch.int16))
+        assert torch.equal(lse.view(torch.int32), ref_l.view(torch.int32))
+    other = make_batch([1, 3], [7000, 900], 8, 2, 128, seed=44)
+    oq, ok_, ov = other.q.to(DEV), other.k.to(DEV), other.v.to(DEV)
+    x = torch.zeros(1, device=DEV)
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g2, stream=s_):
+        x.add_(1.0)
+        with pytest.raises(vp.RaggedPrefillError):
+            vp.ragged_prefill(oq, ok_, ov, other.q_indptr, other.kv_indptr, causal=True)
+    g2.replay()
+    torch.cuda.synchronize()
+    assert float(x.item()) == 1.0
 
 
 def test_graph_capture_replays():

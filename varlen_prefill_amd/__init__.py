@@ -26,7 +26,7 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 from . import _lib
-from ._lib import (RP_SPLIT_ALWAYS, RP_SPLIT_AUTO, RP_SPLIT_NEVER, RaggedPrefillError,
+from ._lib import (RP_SPLIT_ALWAYS, RP_SPLIT_AUTO, RaggedPrefillError,
                    RpPlanInfo, RpPlanOpts)
 
 __all__ = [
@@ -39,7 +39,6 @@ __all__ = [
     "merge_states",
     "RaggedPrefillError",
     "RP_SPLIT_AUTO",
-    "RP_SPLIT_NEVER",
     "RP_SPLIT_ALWAYS",
     "ITEM_FIELDS",
 ]
@@ -132,7 +131,7 @@ class Plan:
                                 1 if self.causal else 0, ctypes.byref(opts), ctypes.byref(handle))
         _lib.check(st, "rp_plan_create")
         self._handle = handle
-        self._workspace = None
+        self._workspaces = {}
 
     @property
     def handle(self) -> ctypes.c_void_p:
@@ -149,6 +148,25 @@ class Plan:
     @property
     def workspace_bytes(self) -> int:
         return int(self._lib.rp_plan_workspace_bytes(self.handle))
+
+    def _workspace_for(self, workspace, device, stream):
+        """(pointer, bytes) of the workspace for one run: the caller's, or
+        one the plan keeps per stream (torch allocates it for that stream), so
+        that runs of one plan enqueued on different streams never share
+        partial states."""
+        import torch
+        need = self.workspace_bytes
+        if workspace is None and need > 0:
+            s = torch.cuda.current_stream(device) if stream is None else stream
+            ws = self._workspaces.get(s.cuda_stream)
+            if ws is None or ws.numel() < need:
+                with torch.cuda.stream(s):
+                    ws = torch.empty(need, dtype=torch.uint8, device=device)
+                self._workspaces[s.cuda_stream] = ws
+            workspace = ws
+        if workspace is None:
+            return None, 0
+        return ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
 
     def items(self) -> np.ndarray:
         n = self.info["num_items"]
@@ -176,13 +194,7 @@ class Plan:
             if (lse.dtype != torch.float32 or lse.device != q.device or not lse.is_contiguous()
                     or tuple(lse.shape[1:]) != (self.num_qo_heads,) or lse.shape[0] < rows_q):
                 raise ValueError("lse must be a contiguous float32 [rows, num_qo_heads] GPU tensor")
-        need = self.workspace_bytes
-        if workspace is None and need > 0:
-            if self._workspace is None or self._workspace.numel() < need:
-                self._workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-            workspace = self._workspace
-        ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
-        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        ws_ptr, ws_bytes = self._workspace_for(workspace, q.device, stream)
         scale = _default_scale(self.head_dim) if sm_scale is None else float(sm_scale)
         st = self._lib.rp_run(self.handle, ctypes.c_void_p(q.data_ptr()),
                               ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
@@ -192,7 +204,7 @@ class Plan:
         _lib.check(st, "rp_run")
         return out, lse
 
-    def _outputs(self, q, out, lse, return_lse, workspace):
+    def _outputs(self, q, out, lse, return_lse, workspace, stream):
         import torch
         rows_q = int(self.q_indptr[-1])
         if out is None:
@@ -203,13 +215,7 @@ class Plan:
             lse = torch.empty((q.shape[0], self.num_qo_heads), dtype=torch.float32, device=q.device)
         if lse is not None:
             _check_lse(lse, rows_q, self.num_qo_heads, q.device)
-        need = self.workspace_bytes
-        if workspace is None and need > 0:
-            if self._workspace is None or self._workspace.numel() < need:
-                self._workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-            workspace = self._workspace
-        ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
-        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        ws_ptr, ws_bytes = self._workspace_for(workspace, q.device, stream)
         return out, lse, ws_ptr, ws_bytes
 
     def run_fp8kv(self, q, k_fp8, v_fp8, k_scale: float, v_scale: float, out=None, lse=None,
@@ -223,7 +229,7 @@ class Plan:
         _check_tensor(q, "q", rows_q, self.num_qo_heads, self.head_dim)
         for name, t in (("k_fp8", k_fp8), ("v_fp8", v_fp8)):
             _check_fp8(t, name, rows_kv, self.num_kv_heads, self.head_dim, 3)
-        out, lse, ws_ptr, ws_bytes = self._outputs(q, out, lse, return_lse, workspace)
+        out, lse, ws_ptr, ws_bytes = self._outputs(q, out, lse, return_lse, workspace, stream)
         scale = _default_scale(self.head_dim) if sm_scale is None else float(sm_scale)
         st = self._lib.rp_run_fp8kv(self.handle, ctypes.c_void_p(q.data_ptr()),
                                     ctypes.c_void_p(k_fp8.data_ptr()), ctypes.c_void_p(v_fp8.data_ptr()),
@@ -250,7 +256,7 @@ class Plan:
                 or block_table.dtype != torch.int32 or block_table.dim() != 2
                 or block_table.shape[0] != self.batch or not block_table.is_contiguous()):
             raise ValueError(f"block_table must be a contiguous int32 [{self.batch}, max_blocks] GPU tensor")
-        out, lse, ws_ptr, ws_bytes = self._outputs(q, out, lse, return_lse, workspace)
+        out, lse, ws_ptr, ws_bytes = self._outputs(q, out, lse, return_lse, workspace, stream)
         scale = _default_scale(self.head_dim) if sm_scale is None else float(sm_scale)
         st = self._lib.rp_run_paged_fp8kv(self.handle, ctypes.c_void_p(q.data_ptr()),
                                           ctypes.c_void_p(k_pages.data_ptr()),
@@ -286,13 +292,7 @@ class Plan:
             if (lse.dtype != torch.float32 or lse.device != q.device or not lse.is_contiguous()
                     or tuple(lse.shape[1:]) != (self.num_qo_heads,) or lse.shape[0] < rows_q):
                 raise ValueError("lse must be a contiguous float32 [rows, num_qo_heads] GPU tensor")
-        need = self.workspace_bytes
-        if workspace is None and need > 0:
-            if self._workspace is None or self._workspace.numel() < need:
-                self._workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-            workspace = self._workspace
-        ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
-        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        ws_ptr, ws_bytes = self._workspace_for(workspace, q.device, stream)
         scale = _default_scale(self.head_dim) if sm_scale is None else float(sm_scale)
         st = self._lib.rp_run_paged(self.handle, ctypes.c_void_p(q.data_ptr()),
                                     ctypes.c_void_p(k_pages.data_ptr()),
@@ -309,7 +309,7 @@ class Plan:
         if self._handle is not None:
             self._lib.rp_plan_destroy(self._handle)
             self._handle = None
-            self._workspace = None
+            self._workspaces = {}
 
     def __del__(self):  # pragma: no cover - best effort
         try:
@@ -349,7 +349,7 @@ class SharedPrefixPlan(Plan):
                                               ctypes.byref(handle))
         _lib.check(st, "rp_plan_create_shared_prefix")
         self._handle = handle
-        self._workspace = None
+        self._workspaces = {}
 
     def run(self, q, k_shared, v_shared, k_unique, v_unique, out=None, lse=None,
             sm_scale: Optional[float] = None, return_lse: bool = True, workspace=None,
@@ -361,7 +361,7 @@ class SharedPrefixPlan(Plan):
         _check_tensor(k_unique, "k_unique", int(self.kv_indptr[-1]), self.num_kv_heads, self.head_dim)
         _check_tensor(v_unique, "v_unique", int(self.kv_indptr[-1]), self.num_kv_heads, self.head_dim)
         out, lse, ws_ptr, ws_bytes, scale = self._shared_outputs(q, out, lse, return_lse, workspace,
-                                                                 sm_scale)
+                                                                 sm_scale, stream)
         st = self._lib.rp_run_shared_prefix(
             self.handle, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_shared.data_ptr()),
             ctypes.c_void_p(v_shared.data_ptr()), ctypes.c_void_p(k_unique.data_ptr()),
@@ -384,7 +384,7 @@ class SharedPrefixPlan(Plan):
         _check_tensor(v_shared, "v_shared", self.shared_kv_len, self.num_kv_heads, self.head_dim)
         _check_pages(k_pages, v_pages, block_table, self.batch, self.num_kv_heads, self.head_dim)
         out, lse, ws_ptr, ws_bytes, scale = self._shared_outputs(q, out, lse, return_lse, workspace,
-                                                                 sm_scale)
+                                                                 sm_scale, stream)
         st = self._lib.rp_run_shared_prefix_paged(
             self.handle, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_shared.data_ptr()),
             ctypes.c_void_p(v_shared.data_ptr()), ctypes.c_void_p(k_pages.data_ptr()),
@@ -395,7 +395,7 @@ class SharedPrefixPlan(Plan):
         _lib.check(st, "rp_run_shared_prefix_paged")
         return out, lse
 
-    def _shared_outputs(self, q, out, lse, return_lse, workspace, sm_scale):
+    def _shared_outputs(self, q, out, lse, return_lse, workspace, sm_scale, stream):
         import torch
         rows_q = int(self.q_indptr[-1])
         if out is None:
@@ -406,13 +406,7 @@ class SharedPrefixPlan(Plan):
             lse = torch.empty((q.shape[0], self.num_qo_heads), dtype=torch.float32, device=q.device)
         if lse is not None:
             _check_lse(lse, rows_q, self.num_qo_heads, q.device)
-        need = self.workspace_bytes
-        if workspace is None and need > 0:
-            if self._workspace is None or self._workspace.numel() < need:
-                self._workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-            workspace = self._workspace
-        ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
-        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        ws_ptr, ws_bytes = self._workspace_for(workspace, q.device, stream)
         scale = _default_scale(self.head_dim) if sm_scale is None else float(sm_scale)
         return out, lse, ws_ptr, ws_bytes, scale
 

@@ -22,7 +22,6 @@ RP_ENOMEM = -3
 RP_EDEVICE = -4
 
 RP_SPLIT_AUTO = 0
-RP_SPLIT_NEVER = 1
 RP_SPLIT_ALWAYS = 2
 
 RP_ITEM_INTS = 16

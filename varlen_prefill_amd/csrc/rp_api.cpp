@@ -348,13 +348,22 @@ struct CachedPlan {
     rp_plan *plan;
 };
 
+// Split-KV workspace of one stream (partial states are written by the tile
+// kernel and read by the merge kernel of the same call, so calls on one
+// stream may share it; calls on different streams may not).
+struct StreamWorkspace {
+    void *stream;
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+
 struct DeviceState {
-    std::list<CachedPlan> plans;  // most recent first
-    void *workspace = nullptr;
-    size_t workspace_bytes = 0;
+    std::list<CachedPlan> plans;             // most recent first
+    std::list<StreamWorkspace> workspaces;   // most recent first
 };
 
 constexpr size_t kPlanCacheSize = 8;
+constexpr size_t kStreamCacheSize = 8;
 std::mutex g_oneshot_mutex;
 std::vector<DeviceState> g_devices;
 
@@ -682,6 +691,11 @@ int ragged_prefill_bf16(const void *q, const void *k, const void *v, void *o, fl
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
         return hip_fail(e, "hipGetDevice");
+    hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(static_cast<hipStream_t>(stream), &capture);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipStreamIsCapturing");
+    const bool capturing = capture != hipStreamCaptureStatusNone;
     std::lock_guard<std::mutex> lock(g_oneshot_mutex);
     if ((int)g_devices.size() <= dev)
         g_devices.resize((size_t)dev + 1);
@@ -700,6 +714,9 @@ int ragged_prefill_bf16(const void *q, const void *k, const void *v, void *o, fl
         }
     }
     if (plan == nullptr) {
+        if (capturing)
+            return fail(RP_EINVAL, "one-shot call under graph capture needs a cached plan: "
+                                   "call once with these offsets outside the capture first");
         int st = create_plan(q_indptr, kv_indptr, batch, num_qo_heads, num_kv_heads, head_dim, cz,
                              nullptr, &plan);
         if (st != RP_OK)
@@ -714,28 +731,57 @@ int ragged_prefill_bf16(const void *q, const void *k, const void *v, void *o, fl
         cp.plan = plan;
         ds.plans.push_front(std::move(cp));
         while (ds.plans.size() > kPlanCacheSize) {
-            // the evicted plan's worklist may still be read by queued work
+            // the evicted plan's worklist may still be read by queued work on any stream
             (void)hipDeviceSynchronize();
             free_plan(ds.plans.back().plan);
             ds.plans.pop_back();
         }
     }
     const size_t need = plan->host.workspace_bytes();
-    if (need > ds.workspace_bytes) {
-        if (ds.workspace) {
-            (void)hipDeviceSynchronize();  // queued work may still use the old workspace
-            (void)hipFree(ds.workspace);
-            ds.workspace = nullptr;
-            ds.workspace_bytes = 0;
+    void *ws = nullptr;
+    size_t ws_bytes = 0;
+    if (need > 0) {
+        auto it = ds.workspaces.begin();
+        for (; it != ds.workspaces.end(); ++it)
+            if (it->stream == stream)
+                break;
+        if (it != ds.workspaces.end())
+            ds.workspaces.splice(ds.workspaces.begin(), ds.workspaces, it);
+        else
+            ds.workspaces.push_front(StreamWorkspace{stream});
+        StreamWorkspace &sw = ds.workspaces.front();
+        if (need > sw.bytes) {
+            if (capturing)
+                return fail(RP_EINVAL, "one-shot call under graph capture needs this stream's "
+                                       "workspace to be large enough: call once with these "
+                                       "offsets on this stream outside the capture first");
+            if (sw.ptr) {
+                // queued work of this stream may still use the old workspace
+                e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+                if (e != hipSuccess)
+                    return hip_fail(e, "hipStreamSynchronize");
+                (void)hipFree(sw.ptr);
+                sw.ptr = nullptr;
+                sw.bytes = 0;
+            }
+            e = hipMalloc(&sw.ptr, need);
+            if (e != hipSuccess) {
+                sw.ptr = nullptr;
+                return fail(RP_ENOMEM, std::string("hipMalloc(workspace): ") + hipGetErrorString(e));
+            }
+            sw.bytes = need;
         }
-        e = hipMalloc(&ds.workspace, need);
-        if (e != hipSuccess) {
-            ds.workspace = nullptr;
-            return fail(RP_ENOMEM, std::string("hipMalloc(workspace): ") + hipGetErrorString(e));
+        ws = sw.ptr;
+        ws_bytes = sw.bytes;
+        while (ds.workspaces.size() > kStreamCacheSize) {
+            // the evicted stream may have been destroyed: wait for the whole device
+            (void)hipDeviceSynchronize();
+            if (ds.workspaces.back().ptr)
+                (void)hipFree(ds.workspaces.back().ptr);
+            ds.workspaces.pop_back();
         }
-        ds.workspace_bytes = need;
     }
-    return run_plan(plan, q, k, v, o, lse, sm_scale, ds.workspace, ds.workspace_bytes, stream);
+    return run_plan(plan, q, k, v, o, lse, sm_scale, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -156,13 +156,9 @@ int build_plan(const int32_t *q_indptr, const int32_t *kv_indptr, const PlanShap
         err = "num_xcds must be in [1, 64] (0 = default)";
         return kEInval;
     }
-    if (shape.split_mode < 0 || shape.split_mode > 2) {
-        err = "unknown split_mode";
+    if (shape.split_mode != 0 && shape.split_mode != 2) {
+        err = "unknown split_mode (0 = auto, 2 = always)";
         return kEInval;
-    }
-    if (shape.split_mode == 1) {
-        err = "split_mode NEVER (in-workgroup chunk folding) is not implemented";
-        return kEUnsupported;
     }
     if (shape.batch > 0 && (q_indptr == nullptr || kv_indptr == nullptr)) {
         err = "q_indptr and kv_indptr must not be NULL when batch > 0";
