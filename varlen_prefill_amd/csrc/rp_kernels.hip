@@ -34,6 +34,7 @@
 // and the natural-log LSE.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <climits>
 #include <cstdint>
 #include <type_traits>
@@ -886,12 +887,19 @@ int launch_tile(const TileArgs &args, int64_t num_items, hipStream_t stream)
 {
     constexpr int lds = tile_lds_bytes<HD, FP8>();
     const void *fn = reinterpret_cast<const void *>(&tile_kernel<HD, PAGED, FP8>);
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    // The dynamic-LDS limit is a per-device function attribute: set it once
+    // per device (devices beyond 64 set it at every launch).
+    static std::atomic<unsigned long long> attr_devices{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return (int)e;
+    const unsigned long long bit = dev >= 0 && dev < 64 ? 1ull << dev : 0ull;
+    if (bit == 0 || (attr_devices.load(std::memory_order_acquire) & bit) == 0) {
+        e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess)
             return (int)e;
-        attr_set = true;
+        attr_devices.fetch_or(bit, std::memory_order_release);
     }
     auto kernel = tile_kernel<HD, PAGED, FP8>;
     hipLaunchKernelGGL(kernel, dim3((unsigned)num_items), dim3(kThreads), lds, stream, args);
