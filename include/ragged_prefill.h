@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define RP_ABI_VERSION 5
+#define RP_ABI_VERSION 6
 
 /* Status codes. */
 enum rp_status {
@@ -180,6 +180,20 @@ int64_t rp_plan_copy_items(const rp_plan *plan, int32_t *dst, int64_t capacity);
 int rp_run(const rp_plan *plan, const void *q, const void *k, const void *v, void *o,
            float *lse, float sm_scale, void *workspace, size_t workspace_bytes,
            void *stream);
+
+/* rp_run for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * kernels, with the split-KV partial states in a fixed array of the library
+ * (a 32 MiB __device__ object that every device the library runs on holds
+ * until the process ends) instead of a caller workspace.  The plan must come
+ * from rp_plan_create (run on this device) and need at most 32 MiB of
+ * workspace (rp_plan_workspace_bytes), else RP_EUNSUPPORTED and nothing is
+ * enqueued; plans without split KV need none.  No allocation, free or host
+ * synchronisation happens in the call.  Calls on one device share the array:
+ * calls that overlap in time (other streams, other host threads) race on it.
+ * Everything else as for rp_run. */
+int rp_run_noalloc(const rp_plan *plan, const void *q, const void *k, const void *v, void *o,
+                   float *lse, float sm_scale, void *stream);
 
 /* Run a plan over PAGED K/V (append prefill over a KV cache; paged KV cache
  * prefill of page "flashinfer-ai/flashinfer", attention API, and the block

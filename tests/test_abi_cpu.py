@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = _lib.load()
-    assert lib.rp_abi_version() == 5
+    assert lib.rp_abi_version() == 6
     for st in (0, -1, -2, -3, -4):
         assert lib.rp_status_string(st)
     assert lib.rp_status_string(12345) == b"unknown status"
@@ -157,3 +157,16 @@ def test_shared_prefix_plan_host_logic():
     vp.SharedPrefixPlan([0, 10], [0, 5], 1, 4, 2, 128, causal=False, host_only=True).close()
     with pytest.raises(vp.RaggedPrefillError):
         vp.SharedPrefixPlan([0, 10], [0, 5], -1, 4, 2, 128, causal=False, host_only=True)
+
+
+def test_noalloc_rejects_plans_beyond_its_array():
+    """rp_run_noalloc refuses, before any device call, a plan whose split-KV
+    workspace exceeds its fixed 32 MiB array."""
+    import ctypes
+    # 64 decode-like requests over 16K keys in 2048-key chunks: 8 partial
+    # states per (request, kv head), 64 KiB each
+    p = _plan([i for i in range(65)], [16384 * i for i in range(65)], hq=32, hkv=8)
+    assert p.workspace_bytes > (32 << 20)
+    st = _lib.load().rp_run_noalloc(p.handle, None, None, None, None, None, ctypes.c_float(1.0), None)
+    assert st == _lib.RP_EUNSUPPORTED
+    assert b"32" in _lib.load().rp_last_error()

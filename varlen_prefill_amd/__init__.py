@@ -204,7 +204,27 @@ class Plan:
         _lib.check(st, "rp_run")
         return out, lse
 
-    def _outputs(self, q, out, lse, return_lse, workspace, stream):
+    def run_noalloc(self, q, k, v, out=None, lse=None, sm_scale: Optional[float] = None,
+                    return_lse: bool = True, stream=None):
+        """run() through rp_run_noalloc: the split-KV partial states live in
+        the library's fixed device array (no workspace; out and lse are
+        allocated here unless given)."""
+        rows_q = int(self.q_indptr[-1])
+        rows_kv = int(self.kv_indptr[-1])
+        _check_tensor(q, "q", rows_q, self.num_qo_heads, self.head_dim)
+        _check_tensor(k, "k", rows_kv, self.num_kv_heads, self.head_dim)
+        _check_tensor(v, "v", rows_kv, self.num_kv_heads, self.head_dim)
+        out, lse, _, _ = self._outputs(q, out, lse, return_lse, None, stream, need_workspace=False)
+        scale = _default_scale(self.head_dim) if sm_scale is None else float(sm_scale)
+        st = self._lib.rp_run_noalloc(self.handle, ctypes.c_void_p(q.data_ptr()),
+                                      ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+                                      ctypes.c_void_p(out.data_ptr()),
+                                      ctypes.c_void_p(lse.data_ptr()) if lse is not None else None,
+                                      ctypes.c_float(scale), _stream_handle(stream))
+        _lib.check(st, "rp_run_noalloc")
+        return out, lse
+
+    def _outputs(self, q, out, lse, return_lse, workspace, stream, need_workspace=True):
         import torch
         rows_q = int(self.q_indptr[-1])
         if out is None:
@@ -215,6 +235,8 @@ class Plan:
             lse = torch.empty((q.shape[0], self.num_qo_heads), dtype=torch.float32, device=q.device)
         if lse is not None:
             _check_lse(lse, rows_q, self.num_qo_heads, q.device)
+        if not need_workspace:
+            return out, lse, None, 0
         ws_ptr, ws_bytes = self._workspace_for(workspace, q.device, stream)
         return out, lse, ws_ptr, ws_bytes
 

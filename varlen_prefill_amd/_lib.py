@@ -38,6 +38,7 @@ EXPORTS = [
     "rp_plan_workspace_bytes",
     "rp_plan_copy_items",
     "rp_run",
+    "rp_run_noalloc",
     "rp_run_paged",
     "rp_run_fp8kv",
     "rp_run_paged_fp8kv",
@@ -110,6 +111,8 @@ def load():
         lib.rp_plan_copy_items.restype = ctypes.c_int64
         lib.rp_run.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, ctypes.c_size_t, P]
         lib.rp_run.restype = I
+        lib.rp_run_noalloc.argtypes = [P, P, P, P, P, P, ctypes.c_float, P]
+        lib.rp_run_noalloc.restype = I
         lib.rp_run_paged.argtypes = [P, P, P, P, P, I, I, P, P, ctypes.c_float, P, ctypes.c_size_t, P]
         lib.rp_run_paged.restype = I
         F = ctypes.c_float

@@ -18,7 +18,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(BUILD, "librp.so")
 INCLUDE = os.path.join(ROOT, "include")
 
-SOURCES = ["rp_kernels.hip", "rp_state_merge.hip", "rp_plan.cpp", "rp_api.cpp"]
+SOURCES = ["rp_kernels.hip", "rp_state_merge.hip", "rp_noalloc.hip", "rp_plan.cpp", "rp_api.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

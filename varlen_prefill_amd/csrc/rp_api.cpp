@@ -16,6 +16,7 @@
 #include <string>
 #include <vector>
 
+#include "rp_api_internal.h"
 #include "rp_internal.h"
 #include "rp_plan.h"
 #include "rp_state_merge.h"
@@ -368,6 +369,19 @@ std::mutex g_oneshot_mutex;
 std::vector<DeviceState> g_devices;
 
 }  // namespace
+
+namespace rp {
+
+int record_error(int status, const char *msg) { return fail(status, msg); }
+
+int run_plan_on(const rp_plan *plan, const void *q, const void *k, const void *v, void *o,
+                float *lse, float sm_scale, void *workspace, size_t workspace_bytes,
+                void *stream)
+{
+    return run_plan(plan, q, k, v, o, lse, sm_scale, workspace, workspace_bytes, stream);
+}
+
+}  // namespace rp
 
 extern "C" {
 
