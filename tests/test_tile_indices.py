@@ -96,3 +96,57 @@ def test_paged_wave_rows_share_one_page(hd):
                 for r in rows:
                     key = kb * bk + min(r, kv_len - 1 - kb * bk)
                     assert key // 16 == key0 // 16
+
+
+def _cycles(addrs, width, group):
+    """LDS cycles beyond the ideal for one wave-wide access: 64 four-byte
+    banks; lanes are served `group` at a time in lane order (16 for 16-byte
+    accesses, 32 for the 8-byte transpose read, the grouping a GPU probe of
+    these access shapes confirmed); within a group, a bank hit by several
+    different dwords costs one cycle per extra dword."""
+    extra = 0
+    for g0 in range(0, 64, group):
+        banks = {}
+        for lane in range(g0, g0 + group):
+            for k in range(width // 4):
+                d = addrs[lane] // 4 + k
+                banks.setdefault(d % 64, set()).add(d)
+        extra += max(len(v) for v in banks.values()) - 1
+    return extra
+
+
+@pytest.mark.parametrize("hd", [128, 256])
+def test_loop_lds_accesses_are_bank_conflict_free(hd):
+    """Bank model of the key loop's LDS traffic: the K-fragment reads
+    (16 bytes per lane) and the V transpose reads (8 bytes per lane) hit
+    every bank at most once per group of lanes served together, and the
+    direct-to-LDS loads write 64 consecutive 16-byte pieces."""
+    bk, _ = _shape(hd)
+    rb = hd * 2
+
+    def swz_k(r):
+        return r & 15
+
+    def swz_v(r):
+        return (r & 3) << 2
+
+    for ds in range(hd // 16):
+        for n in range(bk // 32):
+            addrs = []
+            for lane in range(64):
+                h, qc = lane >> 5, lane & 31
+                row = 32 * n + qc
+                addrs.append(row * rb + 16 * ((2 * ds + h) ^ swz_k(row)))
+            assert _cycles(addrs, 16, 16) == 0, (ds, n)
+    for db in range(hd // 32):
+        for n in range(bk // 32):
+            for t in range(2):
+                for second in (0, 8):
+                    addrs = []
+                    for lane in range(64):
+                        h, grp, s16 = lane >> 5, lane >> 4, lane & 15
+                        row = 32 * n + 16 * t + 4 * h + (s16 >> 2)
+                        cc = 4 * db + 2 * (grp & 1) + ((s16 & 3) >> 1)
+                        addrs.append((row + second) * rb + 16 * (cc ^ swz_v(row)) + 8 * (s16 & 1))
+                    assert _cycles(addrs, 8, 32) == 0, (db, n, t)
+    assert _cycles([16 * lane for lane in range(64)], 16, 16) == 0
