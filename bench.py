@@ -116,48 +116,83 @@ def copy_probe(mib: int) -> None:
     print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 5}))
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(batch, cfg, causal: bool, sm_scale: float, target_s: float) -> dict:
-    """Time the fp64 oracle (as it stands) on a random sample of (token, head)
-    rows of the same workload, on all host cores."""
+    """Time the fp64 oracle (as it stands) on the host cores: the whole batch
+    once on all threads when that fits in about 2.5x target_s, else the
+    batch's leading requests up to about target_s of work; plus a
+    single-thread run of one request of the batch for a per-core rate."""
     import oracle
-    rng = np.random.default_rng(2024)
-    total = int(batch.q_indptr[-1])
-    # request of each token and its visible key count
-    req = np.searchsorted(batch.q_indptr, np.arange(total), side="right") - 1
-    qo = np.diff(batch.q_indptr)[req].astype(np.int64)
-    kv = np.diff(batch.kv_indptr)[req].astype(np.int64)
-    i = np.arange(total) - batch.q_indptr[req]
-    lim = np.clip(i + kv - qo + 1, 0, kv) if causal else kv
+    qo = np.diff(batch.q_indptr).astype(np.int64)
+    kv = np.diff(batch.kv_indptr).astype(np.int64)
 
-    def run(n):
-        toks = rng.integers(0, total, n)
-        heads = rng.integers(0, cfg.num_qo_heads, n)
+    def req_pairs(r):
+        i = np.arange(qo[r])
+        lim = np.clip(i + kv[r] - qo[r] + 1, 0, kv[r]) if causal else np.full(qo[r], kv[r])
+        return float(lim.sum())
+
+    pairs = np.array([req_pairs(r) for r in range(batch.batch)])
+    flops_req = 4.0 * cfg.head_dim * cfg.num_qo_heads * pairs
+
+    def run(n_req):
+        qi, ki = batch.q_indptr[: n_req + 1], batch.kv_indptr[: n_req + 1]
         t0 = time.perf_counter()
-        oracle.ragged_attention_rows(batch.q, batch.k, batch.v, batch.q_indptr, batch.kv_indptr,
-                                     cfg.num_qo_heads, cfg.num_kv_heads, causal, sm_scale, toks, heads)
-        dt = time.perf_counter() - t0
-        flops = float(np.sum(4.0 * cfg.head_dim * lim[toks]))
-        return n, dt, flops
+        oracle.ragged_attention(batch.q, batch.k, batch.v, qi, ki, cfg.num_qo_heads,
+                                cfg.num_kv_heads, causal, sm_scale)
+        return time.perf_counter() - t0
 
-    # calibration: grow the sample until a run takes a tenth of the target,
-    # so that fixed start-up costs do not skew the rate it extrapolates from
-    cap = 2_000_000
-    n, dt, _ = run(256)
-    while dt < 0.1 * target_s and n < cap:
-        n, dt, _ = run(min(cap, n * 8))
-    n_target = int(max(256, min(cap, n * target_s / max(dt, 1e-3))))
-    n, dt, flops = run(n_target)
-    tflops = flops / dt / 1e12
-    flops_per_token = 4.0 * cfg.head_dim * cfg.num_qo_heads * float(np.mean(lim))
+    threads = oracle.num_threads()
+    # rate estimate from the smallest non-empty leading prefix worth timing
+    nz = [r for r in range(batch.batch) if flops_req[r] > 0]
+    if not nz:
+        return None
+    cum = np.cumsum(flops_req)
+    n_cal = int(np.searchsorted(cum, min(cum[-1], 2e9))) + 1
+    rate = cum[n_cal - 1] / max(run(n_cal), 1e-6)
+    if cum[-1] / rate <= 2.5 * target_s:
+        n_req = batch.batch
+    else:
+        n_req = max(1, int(np.searchsorted(cum, rate * target_s)) + 1)
+    dt = run(n_req)
+    flops = float(cum[n_req - 1])
+    toks = int(batch.q_indptr[n_req] - batch.q_indptr[0])
+    sample = (f"the whole batch ({batch.batch} requests)" if n_req == batch.batch else
+              f"requests 0..{n_req - 1} of {batch.batch} (in batch order)")
+    # per-core rate: one request (the one with the least work above 0.1 GFLOP, else the largest) on one thread
+    cand = [r for r in nz if flops_req[r] >= 1e8]
+    r1 = min(cand, key=lambda r: flops_req[r]) if cand else max(nz, key=lambda r: flops_req[r])
+    sub_q = np.array([0, qo[r1]], dtype=np.int32) + batch.q_indptr[r1]
+    sub_kv = np.array([0, kv[r1]], dtype=np.int32) + batch.kv_indptr[r1]
+    oracle.set_num_threads(1)
+    try:
+        t0 = time.perf_counter()
+        oracle.ragged_attention(batch.q, batch.k, batch.v, sub_q, sub_kv, cfg.num_qo_heads,
+                                cfg.num_kv_heads, causal, sm_scale)
+        dt1 = time.perf_counter() - t0
+    finally:
+        oracle.set_num_threads(threads)
     return {
-        "value": tflops,
+        "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": oracle.num_threads(),
+        "cores": threads,
         "kind": "oracle",
-        "sample": f"{n} random (token, qo head) rows of the same batch, {flops / 1e9:.1f} GFLOP, "
-                  f"{dt:.1f} s",
-        "tokens_per_s": tflops * 1e12 / flops_per_token,
+        "sample": f"{sample}: {toks} query tokens, {flops / 1e9:.1f} GFLOP, {dt:.1f} s",
+        "tokens_per_s": toks / dt,
         "seconds": dt,
+        "cpu_model": _cpu_model(),
+        "per_core": {"value": float(flops_req[r1] / dt1 / 1e12), "unit": "TFLOP/s", "threads": 1,
+                     "sample": f"request {r1} ({qo[r1]} query x {kv[r1]} key tokens, "
+                               f"{flops_req[r1] / 1e9:.2f} GFLOP), {dt1:.2f} s"},
     }
 
 
