@@ -284,6 +284,32 @@ def test_one_shot_graph_capture():
     assert float(x.item()) == 1.0
 
 
+def test_injected_allocation_failure_leaves_outputs_untouched(monkeypatch):
+    """RP_FAULT_INJECT=alloc makes the library's device allocations fail: plan
+    creation and a one-shot call that needs a new plan return RP_ENOMEM and
+    leave the outputs as they were; the next call without it works."""
+    import varlen_prefill_amd as vp
+    from varlen_prefill_amd import _lib
+    b = make_batch([1, 40], [5300, 5400], 8, 2, 128, seed=45)
+    q, k, v = b.q.to(DEV), b.k.to(DEV), b.v.to(DEV)
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((q.shape[0], 8), float("nan"), dtype=torch.float32, device=DEV)
+    monkeypatch.setenv("RP_FAULT_INJECT", "alloc")
+    with pytest.raises(vp.RaggedPrefillError) as ei:
+        vp.Plan(b.q_indptr, b.kv_indptr, 8, 2, 128, True)
+    assert ei.value.status == _lib.RP_ENOMEM
+    with pytest.raises(vp.RaggedPrefillError) as ei:
+        vp.ragged_prefill(q, k, v, b.q_indptr, b.kv_indptr, causal=True, out=out, lse=lse)
+    assert ei.value.status == _lib.RP_ENOMEM
+    torch.cuda.synchronize()
+    assert torch.isnan(out).all() and torch.isnan(lse).all()
+    monkeypatch.delenv("RP_FAULT_INJECT")
+    vp.ragged_prefill(q, k, v, b.q_indptr, b.kv_indptr, causal=True, out=out, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = _oracle(b, True, default_scale(128))
+    compare(bf16_to_f64(out.cpu()), lse.cpu().double().numpy(), ro, rl)
+
+
 def test_graph_capture_replays():
     import varlen_prefill_amd as vp
     b = make_batch([150, 20], [900, 20], 8, 2, 128, seed=12)

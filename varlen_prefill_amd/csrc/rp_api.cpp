@@ -83,6 +83,19 @@ void logf(int level, const char *fmt, ...)
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Every device allocation of the library goes through here.  With
+// RP_FAULT_INJECT=alloc in the environment (read at each call) it fails as an
+// exhausted device would, which lets tests drive the RP_ENOMEM paths.
+hipError_t device_alloc(void **p, size_t n)
+{
+    const char *f = std::getenv("RP_FAULT_INJECT");
+    if (f != nullptr && std::strcmp(f, "alloc") == 0) {
+        *p = nullptr;
+        return hipErrorOutOfMemory;
+    }
+    return hipMalloc(p, n);
+}
+
 int hip_fail(hipError_t e, const char *what)
 {
     return fail(RP_EDEVICE, std::string(what) + ": " + hipGetErrorString(e));
@@ -95,7 +108,7 @@ int upload_plan(rp_plan *p)
         return hip_fail(e, "hipGetDevice");
     if (!p->host.items.empty()) {
         const size_t n = p->host.items.size() * sizeof(rp::Item);
-        e = hipMalloc(reinterpret_cast<void **>(&p->d_items), n);
+        e = device_alloc(reinterpret_cast<void **>(&p->d_items), n);
         if (e != hipSuccess)
             return fail(RP_ENOMEM, std::string("hipMalloc(worklist): ") + hipGetErrorString(e));
         e = hipMemcpy(p->d_items, p->host.items.data(), n, hipMemcpyHostToDevice);
@@ -104,7 +117,7 @@ int upload_plan(rp_plan *p)
     }
     if (!p->host.merges.empty()) {
         const size_t n = p->host.merges.size() * sizeof(rp::MergeItem);
-        e = hipMalloc(reinterpret_cast<void **>(&p->d_merges), n);
+        e = device_alloc(reinterpret_cast<void **>(&p->d_merges), n);
         if (e != hipSuccess)
             return fail(RP_ENOMEM, std::string("hipMalloc(merge list): ") + hipGetErrorString(e));
         e = hipMemcpy(p->d_merges, p->host.merges.data(), n, hipMemcpyHostToDevice);
@@ -366,7 +379,14 @@ struct DeviceState {
 constexpr size_t kPlanCacheSize = 8;
 constexpr size_t kStreamCacheSize = 8;
 std::mutex g_oneshot_mutex;
-std::vector<DeviceState> g_devices;
+// Cached plans and workspaces live until the process ends.  The holder is
+// never destroyed, so nothing is freed during static destruction (when the
+// HIP runtime may already be gone) and the memory stays reachable.
+std::vector<DeviceState> &device_states()
+{
+    static auto *states = new std::vector<DeviceState>();
+    return *states;
+}
 
 }  // namespace
 
@@ -711,9 +731,10 @@ int ragged_prefill_bf16(const void *q, const void *k, const void *v, void *o, fl
         return hip_fail(e, "hipStreamIsCapturing");
     const bool capturing = capture != hipStreamCaptureStatusNone;
     std::lock_guard<std::mutex> lock(g_oneshot_mutex);
-    if ((int)g_devices.size() <= dev)
-        g_devices.resize((size_t)dev + 1);
-    DeviceState &ds = g_devices[(size_t)dev];
+    std::vector<DeviceState> &devices = device_states();
+    if ((int)devices.size() <= dev)
+        devices.resize((size_t)dev + 1);
+    DeviceState &ds = devices[(size_t)dev];
     const int cz = causal ? 1 : 0;
     rp_plan *plan = nullptr;
     for (auto it = ds.plans.begin(); it != ds.plans.end(); ++it) {
@@ -778,7 +799,7 @@ int ragged_prefill_bf16(const void *q, const void *k, const void *v, void *o, fl
                 sw.ptr = nullptr;
                 sw.bytes = 0;
             }
-            e = hipMalloc(&sw.ptr, need);
+            e = device_alloc(&sw.ptr, need);
             if (e != hipSuccess) {
                 sw.ptr = nullptr;
                 return fail(RP_ENOMEM, std::string("hipMalloc(workspace): ") + hipGetErrorString(e));
