@@ -1,11 +1,12 @@
 """Host-side check of the tile kernel's staging and LDS index arithmetic.
 
 Restates, for every tile shape the library compiles (head_dim 128 and 256 with
-their key-block sizes and pipeline depths), the mapping of direct-to-LDS load
-lanes to K/V chunks and the K-row and V-transpose read addresses, and checks
-that every LDS access stays inside its buffer and every chunk of a block is
-written exactly once.  Runs without a GPU; a failure here means a kernel
-change would read or write LDS out of bounds.
+their key-block sizes, pipeline depths and wave layouts: 4 waves of 32 rows at
+head_dim 128, 8 waves of 16 rows at 256), the mapping of direct-to-LDS load
+lanes to K/V chunks and the K-row, V-transpose and epilogue addresses, and
+checks that every LDS access stays inside its buffer and every chunk of a
+block is written exactly once.  Runs without a GPU; a failure here means a
+kernel change would read or write LDS out of bounds.
 """
 
 import os
@@ -23,10 +24,72 @@ def _shape(hd):
     return bk, st
 
 
+def _waves(hd):
+    """(rows per wave, waves per workgroup) of the tile kernel at head_dim hd"""
+    rpw = 32 if hd == 128 else 16
+    return rpw, 128 // rpw
+
+
+def swz_k(r):
+    return r & 15
+
+
+def _swz_v(hd):
+    return (lambda r: (r & 3) << 2) if hd == 128 else (lambda r: (r & 7) << 1)
+
+
+def _k_reads(hd, bk):
+    """(row, 16-byte position) of every K-fragment read, per lane, in issue groups"""
+    rpw, _ = _waves(hd)
+    out = []
+    if rpw == 32:
+        for ds in range(hd // 16):
+            for n in range(bk // 32):
+                out.append([(32 * n + (lane & 31), (2 * ds + (lane >> 5)) ^ swz_k(32 * n + (lane & 31)))
+                            for lane in range(64)])
+    else:
+        for ks in range(hd // 32):
+            for t in range(2):
+                out.append([(16 * t + (lane & 15), (4 * ks + (lane >> 4)) ^ swz_k(16 * t + (lane & 15)))
+                            for lane in range(64)])
+    return out
+
+
+def _v_reads(hd, bk):
+    """byte address of every 8-byte V transpose read, per lane, in issue groups"""
+    rpw, _ = _waves(hd)
+    rb, swz_v = hd * 2, _swz_v(hd)
+    out = []
+    if rpw == 32:
+        for db in range(hd // 32):
+            for n in range(bk // 32):
+                for t in range(2):
+                    for second in (0, 8):
+                        addrs = []
+                        for lane in range(64):
+                            h, grp, s16 = lane >> 5, lane >> 4, lane & 15
+                            row = 32 * n + 16 * t + 4 * h + (s16 >> 2)
+                            cc = 4 * db + 2 * (grp & 1) + ((s16 & 3) >> 1)
+                            addrs.append((row + second, (row + second) * rb + 16 * (cc ^ swz_v(row)) + 8 * (s16 & 1)))
+                        out.append(addrs)
+    else:
+        for dt in range(hd // 16):
+            for u in range(2):
+                addrs = []
+                for lane in range(64):
+                    j, n16 = lane >> 4, lane & 15
+                    row = 16 * u + 4 * j + (n16 >> 2)
+                    cc = 2 * dt + ((n16 & 3) >> 1)
+                    addrs.append((row, row * rb + 16 * (cc ^ swz_v(row)) + 8 * (n16 & 1)))
+                out.append(addrs)
+    return out
+
+
 @pytest.mark.parametrize("hd", [128, 256])
 def test_staging_and_reads_stay_in_bounds(hd):
     bk, stages = _shape(hd)
-    threads = 256
+    rpw, nw = _waves(hd)
+    threads = 64 * nw
     rb, cpr = hd * 2, hd // 8
     tile = bk * rb
     nload = tile // 1024 // (threads // 64)
@@ -34,12 +97,7 @@ def test_staging_and_reads_stay_in_bounds(hd):
     stage = 2 * tile
     lds = stages * stage
     assert lds <= 160 * 1024
-
-    def swz_k(r):
-        return r & 15
-
-    def swz_v(r):
-        return (r & 3) << 2
+    swz_v = _swz_v(hd)
 
     wk, wv = set(), set()
     for w in range(threads // 64):
@@ -56,23 +114,48 @@ def test_staging_and_reads_stay_in_bounds(hd):
                 wv.add((rr, pp ^ swz_v(rr)))
     assert len(wk) == bk * cpr and len(wv) == bk * cpr
 
-    nb, ds_steps, dblocks = bk // 32, hd // 16, hd // 32
+    for group in _k_reads(hd, bk):
+        for row, pos in group:
+            assert row < bk and 0 <= pos < cpr
+            assert row * rb + 16 * pos + 16 <= tile
+    for group in _v_reads(hd, bk):
+        for row, addr in group:
+            assert row < bk and addr + 8 <= tile
+    # epilogue: each wave's rows of O (bf16) or of one half of a partial
+    # state (fp32), through the freed K/V stages
+    for row_bytes in (rb, 2 * hd):
+        assert nw * rpw * row_bytes <= lds
+
+
+@pytest.mark.parametrize("hd", [256])
+def test_16_row_epilogue_writes_cover_each_row_once(hd):
+    """16-row waves write O as 8-byte halves of 16-byte chunks: lanes part and
+    part ^ 1 fill chunk 2 dt + part // 2 of row n16; every byte of the wave's
+    rows is written exactly once, and the fp32 passes likewise."""
+    rpw, _ = _waves(hd)
+    rb, cpr = hd * 2, hd // 8
+    seen = {}
     for lane in range(64):
-        h, qc, grp, s16 = lane >> 5, lane & 31, lane >> 4, lane & 15
-        for ds in range(ds_steps):
-            for n in range(nb):
-                row = 32 * n + qc
-                pos = (2 * ds + h) ^ swz_k(row)
-                assert row < bk and 0 <= pos < cpr
-                assert row * rb + 16 * pos + 16 <= tile
-        for db in range(dblocks):
-            for n in range(nb):
-                for t in range(2):
-                    row = 32 * n + 16 * t + 4 * h + (s16 >> 2)
-                    cc = 4 * db + 2 * (grp & 1) + ((s16 & 3) >> 1)
-                    pos = cc ^ swz_v(row)
-                    assert 0 <= pos < cpr and row + 8 < bk
-                    assert (row + 8) * rb + 16 * pos + 8 * (s16 & 1) + 8 <= tile
+        n16, part = lane & 15, lane >> 4
+        for dt in range(hd // 16):
+            cc = 2 * dt + (part >> 1)
+            off = n16 * rb + 16 * (cc ^ (n16 & (cpr - 1))) + 8 * (part & 1)
+            for b in range(8):
+                assert off + b not in seen
+                seen[off + b] = 1
+    assert len(seen) == rpw * rb
+    cprf = hd // 8
+    for _pass in range(2):
+        seen = set()
+        for lane in range(64):
+            n16, part = lane & 15, lane >> 4
+            for dtl in range(hd // 32):
+                cc = 4 * dtl + part
+                off = n16 * cprf * 16 + 16 * (cc ^ (n16 & (cprf - 1)))
+                assert off + 16 <= rpw * cprf * 16
+                assert off not in seen
+                seen.add(off)
+        assert len(seen) == rpw * cprf
 
 
 @pytest.mark.parametrize("hd", [128, 256])
@@ -82,7 +165,8 @@ def test_paged_wave_rows_share_one_page(hd):
     every row a wave's loads touch lies in the same 16-key-aligned group as
     that key, also after clamping rows past the request's end."""
     bk, _ = _shape(hd)
-    threads = 256
+    _, nw = _waves(hd)
+    threads = 64 * nw
     rb, cpr = hd * 2, hd // 8
     nload = bk * rb // 1024 // (threads // 64)
     wave_rows = nload * 1024 // rb
@@ -123,30 +207,29 @@ def test_loop_lds_accesses_are_bank_conflict_free(hd):
     direct-to-LDS loads write 64 consecutive 16-byte pieces."""
     bk, _ = _shape(hd)
     rb = hd * 2
-
-    def swz_k(r):
-        return r & 15
-
-    def swz_v(r):
-        return (r & 3) << 2
-
-    for ds in range(hd // 16):
-        for n in range(bk // 32):
-            addrs = []
-            for lane in range(64):
-                h, qc = lane >> 5, lane & 31
-                row = 32 * n + qc
-                addrs.append(row * rb + 16 * ((2 * ds + h) ^ swz_k(row)))
-            assert _cycles(addrs, 16, 16) == 0, (ds, n)
-    for db in range(hd // 32):
-        for n in range(bk // 32):
-            for t in range(2):
-                for second in (0, 8):
-                    addrs = []
-                    for lane in range(64):
-                        h, grp, s16 = lane >> 5, lane >> 4, lane & 15
-                        row = 32 * n + 16 * t + 4 * h + (s16 >> 2)
-                        cc = 4 * db + 2 * (grp & 1) + ((s16 & 3) >> 1)
-                        addrs.append((row + second) * rb + 16 * (cc ^ swz_v(row)) + 8 * (s16 & 1))
-                    assert _cycles(addrs, 8, 32) == 0, (db, n, t)
+    for i, group in enumerate(_k_reads(hd, bk)):
+        assert _cycles([row * rb + 16 * pos for row, pos in group], 16, 16) == 0, i
+    for i, group in enumerate(_v_reads(hd, bk)):
+        assert _cycles([addr for _, addr in group], 8, 32) == 0, i
     assert _cycles([16 * lane for lane in range(64)], 16, 16) == 0
+
+
+def test_16_row_epilogue_lds_writes_are_bank_conflict_free():
+    """head_dim 256: the 8-byte O writes (lanes part and part ^ 1 fill one
+    16-byte chunk) and the 16-byte fp32 partial-state writes"""
+    hd = 256
+    rb, cpr = hd * 2, hd // 8
+    for dt in range(hd // 16):
+        addrs = []
+        for lane in range(64):
+            n16, part = lane & 15, lane >> 4
+            cc = 2 * dt + (part >> 1)
+            addrs.append(n16 * rb + 16 * (cc ^ (n16 & (cpr - 1))) + 8 * (part & 1))
+        assert _cycles(addrs, 8, 32) == 0, dt
+    for dtl in range(hd // 32):
+        addrs = []
+        for lane in range(64):
+            n16, part = lane & 15, lane >> 4
+            cc = 4 * dtl + part
+            addrs.append(n16 * cpr * 16 + 16 * (cc ^ (n16 & (cpr - 1))))
+        assert _cycles(addrs, 16, 16) == 0, dtl

@@ -21,8 +21,7 @@
 
 namespace rp {
 
-constexpr int kTileRows = 128;      // rows per tile: 4 waves x 32 rows
-constexpr int kThreads = 256;       // threads per tile workgroup
+constexpr int kTileRows = 128;      // rows per tile: 4 waves x 32 rows (head_dim 128), 8 x 16 (256)
 constexpr int kMergeThreads = 256;  // threads per merge workgroup
 constexpr int kDefaultKvChunk = 8192;
 constexpr int kChunkAlign = 64;     // kv_chunk must be a multiple of this

@@ -47,6 +47,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -58,12 +59,22 @@ constexpr float kRescaleLog2 = 8.0f;
 // the reference max (fast path of the softmax update)
 constexpr float kFastSumMax = 128.0f;
 
+// Wave layout.  head_dim 128: 4 waves of 32 rows (32x32x16 MFMAs), two
+// workgroups per CU.  head_dim 256: 8 waves of 16 rows (16x16x32 MFMAs), one
+// workgroup per CU.  Both run two waves per SIMD, so that one wave's softmax
+// and LDS latency overlap the other's MFMAs; at head_dim 256 32-row waves
+// would need about twice the registers and leave one wave per SIMD.
 template <int HD>
 struct Tile {
+    static constexpr int RPW = HD == 128 ? 32 : 16;   // tile rows per wave
+    static constexpr int NW = kTileRows / RPW;         // waves per workgroup
+    static constexpr int THREADS = 64 * NW;
     static constexpr int BK = key_block(HD);     // keys per block
-    static constexpr int NB = BK / 32;           // 32-key MFMA row blocks of S^T
-    static constexpr int DS = HD / 16;           // k-steps of the QK^T MFMA
-    static constexpr int DB = HD / 32;           // 32-wide d blocks of O^T
+    static constexpr int NB = BK / 32;           // 32-key MFMA row blocks of S^T (32-row waves)
+    static constexpr int DS = HD / 16;           // k-steps of the QK^T MFMA (32-row waves)
+    static constexpr int DB = HD / 32;           // 32-wide d blocks of O^T (32-row waves)
+    static constexpr int KS16 = HD / 32;         // k-steps of the QK^T MFMA (16-row waves)
+    static constexpr int DT16 = HD / 16;         // 16-wide d tiles of O^T (16-row waves)
     static constexpr int RB = HD * 2;            // bytes per K/V row in LDS (unpadded)
     static constexpr int CPR = HD / 8;           // 16-byte chunks per row
     static constexpr int TILE_BYTES = BK * RB;   // one K (or V) block
@@ -71,19 +82,23 @@ struct Tile {
     static constexpr int STAGES = kv_stages(HD);           // blocks in flight
     static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
     // direct-to-LDS loads: one instruction moves 64 lanes x 16 bytes
-    static constexpr int NLOAD = TILE_BYTES / (64 * 16) / (kThreads / 64);
-    static_assert(NLOAD * 64 * 16 * (kThreads / 64) == TILE_BYTES, "block must split evenly over waves");
+    static constexpr int NLOAD = TILE_BYTES / (64 * 16) / NW;
+    static_assert(NLOAD * 64 * 16 * NW == TILE_BYTES, "block must split evenly over waves");
+    static_assert(RPW == 32 || BK == 32, "16-row waves take a 32-key block as one PV k-step");
 };
 
 // LDS layout: chunk c (16 bytes) of key row r sits at chunk position
 // c ^ swz(r) of that row (rows are 256 or 512 bytes, a multiple of the 64
 // four-byte banks).  K is read 16 rows at a time at one chunk (128-bit reads
 // are served 16 lanes per cycle): swizzle r & 15 puts those rows on distinct
-// 16-byte slots.  V is read by the transpose read, 32 lanes per cycle over 4
-// rows x 4 adjacent chunks: swizzle 4 (r & 3) moves each row to its own
-// 4-chunk group.
+// 16-byte slots.  V is read by the transpose read, 32 lanes per cycle: with
+// 32-row waves (head_dim 128) over 4 rows x 4 adjacent chunks, where swizzle
+// 4 (r & 3) moves each row to its own 4-chunk group; with 16-row waves
+// (head_dim 256) over 8 rows x 2 adjacent chunks, where swizzle 2 (r & 7)
+// moves each row to its own chunk pair.
 __device__ inline int swz_k(int r) { return r & 15; }
-__device__ inline int swz_v(int r) { return (r & 3) << 2; }
+template <int HD>
+__device__ inline int swz_v(int r) { return HD == 128 ? (r & 3) << 2 : (r & 7) << 1; }
 
 __device__ inline float pair_max(float x)
 {
@@ -101,6 +116,32 @@ __device__ inline float pair_sum(float x)
                                               __builtin_bit_cast(unsigned, x), false, false);
     return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
+
+// 16-row waves: lanes l, l^16, l^32, l^48 hold the four parts of one row's
+// keys.  Every lane computes (x0 op x1) op (x2 op x3) and gets the same bits.
+__device__ inline float quad_max(float x)
+{
+    auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x),
+                                              __builtin_bit_cast(unsigned, x), false, false);
+    const float y = fmaxf(__builtin_bit_cast(float, (unsigned)a[0]), __builtin_bit_cast(float, (unsigned)a[1]));
+    auto b = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, y),
+                                              __builtin_bit_cast(unsigned, y), false, false);
+    return fmaxf(__builtin_bit_cast(float, (unsigned)b[0]), __builtin_bit_cast(float, (unsigned)b[1]));
+}
+
+__device__ inline float quad_sum(float x)
+{
+    auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x),
+                                              __builtin_bit_cast(unsigned, x), false, false);
+    const float y = __builtin_bit_cast(float, (unsigned)a[0]) + __builtin_bit_cast(float, (unsigned)a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, y),
+                                              __builtin_bit_cast(unsigned, y), false, false);
+    return __builtin_bit_cast(float, (unsigned)b[0]) + __builtin_bit_cast(float, (unsigned)b[1]);
+}
+
+// the row sum of the lanes' parts, in the wave layout of head_dim HD
+template <int HD>
+__device__ inline float row_sum(float x) { return Tile<HD>::RPW == 32 ? pair_sum(x) : quad_sum(x); }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -127,12 +168,21 @@ __device__ inline void fold_state(float &lse_a, float (&o_a)[N], float lse_b, co
 }
 
 // Registers one wave carries through a tile.
-template <int HD>
+template <int HD, bool R16 = (Tile<HD>::RPW == 16)>
 struct WaveState {
     bf16x8 qf[Tile<HD>::DS];   // Q fragments (B operand of S^T = K Q^T)
     f32x16 acc[Tile<HD>::DB];  // O^T accumulators
     float m;                   // running max of scaled scores (log2 units)
     float l;                   // this lane's part of the running sum
+};
+
+// 16-row waves
+template <int HD>
+struct WaveState<HD, true> {
+    bf16x8 qf[Tile<HD>::KS16];  // Q fragments, 32 d per k-step
+    f32x4 acc[Tile<HD>::DT16];  // O^T accumulators, 16 d per tile
+    float m;
+    float l;
 };
 
 // One key block of one wave: S^T = K Q^T, mask, online softmax update,
@@ -188,7 +238,7 @@ __device__ __attribute__((always_inline)) inline void block_step(
                 // 16 (grp & 1) + 4 (s16 & 3): chunk c, byte 8 (s16 & 1) within it
                 const int row = 32 * n + 16 * t + 4 * h + (s16 >> 2);
                 const int cc = 4 * db + 2 * (grp & 1) + ((s16 & 3) >> 1);
-                const char *vp = Vs + row * T::RB + 16 * (cc ^ swz_v(row)) + 8 * (s16 & 1);
+                const char *vp = Vs + row * T::RB + 16 * (cc ^ swz_v<HD>(row)) + 8 * (s16 & 1);
                 const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (lds_i16x4 *)((__attribute__((address_space(3))) char *)vp));
                 const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -377,19 +427,193 @@ __device__ __attribute__((always_inline)) inline void block_step(
     }
 }
 
+// One key block of one 16-row wave (head_dim 256): the same steps as
+// block_step with 16x16x32 MFMAs.  Lane (n16 = lane % 16, j = lane / 16)
+// holds row n16 of the wave.
+//   S^T = K Q^T: two 16-key tiles t; k-step ks covers d 32 ks .. 32 ks + 31,
+//     lane part j holding d 32 ks + 8 j .. + 7 of its key (A) and row (B);
+//     the result's register i of tile t is key 16 t + 4 j + i.
+//   O^T += V^T P^T: one k-step over the 32 keys; lane part j holds, as its
+//     8 k-values, keys 4 j + e and 16 + 4 j + e (e < 4): exactly its own
+//     S^T registers, so P never leaves the lane; the A operand (V^T, d tile
+//     dt: d = 16 dt + n16) takes the same keys with two transpose reads.
+// thr: this lane's visible-key bound relative to the block start and 4 j.
+template <int HD, bool POS_SCALE, bool MASK, bool FORCE>
+__device__ __attribute__((always_inline)) inline void block_step16(
+    WaveState<HD> &st, const char *Ks, const char *Vs, float c, int thr, bool valid, bool trig,
+    float kappa, int n16, int j)
+{
+    using T = Tile<HD>;
+    constexpr int KS = T::KS16;
+    constexpr int DT = T::DT16;
+    f32x4 s[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            s[t][i] = 0.0f;
+    bf16x8 kf[KS][2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int row = 16 * t + n16;
+            kf[ks][t] = *reinterpret_cast<const bf16x8 *>(Ks + row * T::RB + 16 * ((4 * ks + j) ^ swz_k(row)));
+        }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+            s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks][t], st.qf[ks], s[t], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // V fragments of the first half of the d tiles, requested now so that
+    // they arrive during the softmax (the second half is requested after the
+    // first half's PV MFMAs are issued).  In each 16-lane group, source lane
+    // n16 reads key row 16 u + 4 j + n16 / 4 at d = 16 dt + 4 (n16 % 4): lane
+    // n16 then receives V[16 u + 4 j + e][16 dt + n16] for e = 0..3.
+    auto read_v = [&](int dt) __attribute__((always_inline)) {
+        i16x4 v[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int row = 16 * u + 4 * j + (n16 >> 2);
+            const int cc = 2 * dt + ((n16 & 3) >> 1);
+            const char *vp = Vs + row * T::RB + 16 * (cc ^ swz_v<HD>(row)) + 8 * (n16 & 1);
+            v[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4 *)((__attribute__((address_space(3))) char *)vp));
+        }
+        const i16x8 v01 = __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_bit_cast(bf16x8, v01);
+    };
+    constexpr int DH = DT / 2;
+    bf16x8 vf[DT];
+#pragma unroll
+    for (int dt = 0; dt < DH; ++dt)
+        vf[dt] = read_v(dt);
+    __builtin_amdgcn_sched_barrier(0);
+    // p[4 t + i]: key 16 t + 4 j + i
+    float p[8];
+    float tsum;
+    auto exp_sum = [&](float m_use) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float x = POS_SCALE ? __builtin_fmaf(s[t][i], c, -m_use) : s[t][i] - m_use;
+                p[4 * t + i] = fast_exp2(x);
+            }
+        tsum = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    };
+    // Lazy rescale, fast path and the split of P exactly as in block_step;
+    // the row's parts sit in four lanes instead of two.
+    constexpr bool FAST = POS_SCALE;
+    bool full = true;
+    bool check = !FORCE && trig;
+    if (FAST) {
+        if (MASK) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (16 * t + i >= thr)
+                        s[t][i] = -INFINITY;
+        }
+        const float lim_t = valid ? kappa * st.l : INFINITY;
+        exp_sum(st.m);
+        full = __any(!(tsum <= kFastSumMax));
+        if (!FORCE)
+            check = __any(tsum > lim_t);
+    }
+    if (__builtin_expect(full, !FAST)) {
+        float mx = -INFINITY;
+        if (POS_SCALE) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (!FAST && MASK && 16 * t + i >= thr)
+                        s[t][i] = -INFINITY;
+                    mx = fmaxf(mx, s[t][i]);
+                }
+            mx = quad_max(mx) * c;
+        } else {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float x = s[t][i] * c;
+                    if (MASK && 16 * t + i >= thr)
+                        x = -INFINITY;
+                    s[t][i] = x;
+                    mx = fmaxf(mx, x);
+                }
+            mx = quad_max(mx);
+        }
+        const bool grow = mx > st.m + kRescaleLog2;
+        const float m_ref = grow ? mx : st.m;
+        const float m_use = m_ref == -INFINITY ? 0.0f : m_ref;
+        exp_sum(m_use);
+        if (__any(grow)) {
+            const float alpha = fast_exp2(st.m - m_use);
+            st.l *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    st.acc[dt][i] *= alpha;
+        }
+        st.m = m_ref;
+        check = !FORCE && trig;
+    }
+    st.l += tsum;
+    bool split = FORCE;
+    if (!FORCE && __builtin_expect(check, !FAST)) {
+        float pm = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            pm = fmaxf(pm, p[e]);
+        split = __any(valid && pm > kHiLoFracPartial * quad_sum(st.l));
+    }
+    bf16x8 ph;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        ph[e] = (__bf16)p[e];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int dt = 0; dt < DH; ++dt)
+        st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], ph, st.acc[dt], 0, 0, 0);
+#pragma unroll
+    for (int dt = DH; dt < DT; ++dt)
+        vf[dt] = read_v(dt);
+#pragma unroll
+    for (int dt = DH; dt < DT; ++dt)
+        st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], ph, st.acc[dt], 0, 0, 0);
+    if (__builtin_expect(split, 0)) {
+        bf16x8 pl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            pl[e] = (__bf16)(p[e] - (float)ph[e]);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+            st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pl, st.acc[dt], 0, 0, 0);
+    }
+}
+
 template <int HD, bool POS_SCALE, bool PAGED, bool FP8>
 __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
 {
     using T = Tile<HD>;
+    constexpr bool R16 = T::RPW == 16;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
-    const int h = lane >> 5;          // which half of the wave
-    const int qc = lane & 31;         // MFMA column = the wave's row
+    const int qc = lane & (T::RPW - 1);   // the lane's row within the wave (MFMA column)
+    const int part = lane / T::RPW;       // which part of the row's keys and d the lane holds
+    const int h = lane >> 5;
     const int grp = lane >> 4;
     const int s16 = lane & 15;
     const int g = a.group;
-    const int r = w * 32 + qc;        // tile row
+    const int r = w * T::RPW + qc;        // tile row
     const int tok = r / g;
     const int hig = r - tok * g;
     const bool row_valid = tok < it.n_tok;
@@ -429,7 +653,7 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
         const int pp = chunk - rr * T::CPR;
         grow = rr;
         kc = 8 * (pp ^ swz_k(rr));
-        vc = 8 * (pp ^ swz_v(rr));
+        vc = 8 * (pp ^ swz_v<HD>(rr));
     };
     constexpr bool KEEP_OFFSETS = HD == 128 || !PAGED;
     int grow_[T::NLOAD], kcol[T::NLOAD], vcol[T::NLOAD];
@@ -536,9 +760,11 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
     // scale (k_scale) and the final normalisation (v_scale).  A wave's 8
     // rows are aligned consecutive keys, so paging keeps one page id per
     // wave and block.  Staging: K of wave w at 8 HD w, V at BK HD + 8 HD w.
+    constexpr int F8_W = T::BK / T::NW;        // key rows per wave and block
     constexpr int F8_CPR = HD / 16;            // 16-byte chunks per fp8 row
     constexpr int F8_RPL = 64 / F8_CPR;        // rows per load instruction
-    constexpr int F8_NL = 8 / F8_RPL;          // load instructions per wave and tensor
+    constexpr int F8_NL = F8_W / F8_RPL;       // load instructions per wave and tensor
+    static_assert(F8_NL * F8_RPL == F8_W, "fp8 rows must split evenly over a wave's loads");
     auto issue_fp8 = [&](int kb) __attribute__((always_inline)) {
         const int kv_stride_b = a.num_kv_heads * HD;   // bytes between fp8 key rows
         const size_t head_b = ((size_t)(PAGED ? 0 : it.kv_row0) * a.num_kv_heads + it.kv_head) * HD;
@@ -548,13 +774,13 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
         const char *vp = static_cast<const char *>(a.v) + head_b + blk;
 #pragma unroll
         for (int i = 0; i < F8_NL; ++i) {
-            const int f8_row = wu * 8 + i * F8_RPL + lane / F8_CPR;   // this lane's key row in the block
+            const int f8_row = wu * F8_W + i * F8_RPL + lane / F8_CPR;   // this lane's key row in the block
             const int f8_chunk = lane % F8_CPR;                         // its 16-byte chunk (16 elements)
             int row = min(f8_row, it.kv_len - 1 - kb * T::BK);
             if (PAGED)
                 row = (kb * T::BK + row) & page_mask;
             const unsigned off = (unsigned)(row * kv_stride_b + 16 * f8_chunk);
-            const unsigned dst = lds_base + (unsigned)(T::STAGES * T::STAGE_BYTES + wu * 8 * HD + i * 1024);
+            const unsigned dst = lds_base + (unsigned)(T::STAGES * T::STAGE_BYTES + wu * F8_W * HD + i * 1024);
             asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                          :: "s"(dst), "v"(off), "s"(kp) : "memory", "m0");
             asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
@@ -574,9 +800,9 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
         };
 #pragma unroll
         for (int i = 0; i < F8_NL; ++i) {
-            const int f8_row = wu * 8 + i * F8_RPL + lane / F8_CPR;
+            const int f8_row = wu * F8_W + i * F8_RPL + lane / F8_CPR;
             const int f8_chunk = lane % F8_CPR;
-            const char *src = smem + T::STAGES * T::STAGE_BYTES + wu * 8 * HD + i * 1024 + 16 * lane;
+            const char *src = smem + T::STAGES * T::STAGE_BYTES + wu * F8_W * HD + i * 1024 + 16 * lane;
             const u32x4 kq = *reinterpret_cast<const u32x4 *>(src);
             const u32x4 vq = *reinterpret_cast<const u32x4 *>(src + T::BK * HD);
             char *Kd = smem + buf * T::STAGE_BYTES + f8_row * T::RB;
@@ -584,8 +810,8 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
             const int c0 = 2 * f8_chunk;
             *reinterpret_cast<bf16x8 *>(Kd + 16 * (c0 ^ swz_k(f8_row))) = cvt8(kq[0], kq[1]);
             *reinterpret_cast<bf16x8 *>(Kd + 16 * ((c0 + 1) ^ swz_k(f8_row))) = cvt8(kq[2], kq[3]);
-            *reinterpret_cast<bf16x8 *>(Vd + 16 * (c0 ^ swz_v(f8_row))) = cvt8(vq[0], vq[1]);
-            *reinterpret_cast<bf16x8 *>(Vd + 16 * ((c0 + 1) ^ swz_v(f8_row))) = cvt8(vq[2], vq[3]);
+            *reinterpret_cast<bf16x8 *>(Vd + 16 * (c0 ^ swz_v<HD>(f8_row))) = cvt8(vq[0], vq[1]);
+            *reinterpret_cast<bf16x8 *>(Vd + 16 * ((c0 + 1) ^ swz_v<HD>(f8_row))) = cvt8(vq[2], vq[3]);
         }
     };
 
@@ -609,13 +835,15 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
     first_loads();
 
     WaveState<HD> st;
+    constexpr int NQF = R16 ? T::KS16 : T::DS;   // Q fragments
     {
+        // lane part `part` holds d (16 or 32) ds + 8 part .. + 7 of its row
         const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(
-            static_cast<const __bf16 *>(a.q) + q_row * HD + 8 * h);
+            static_cast<const __bf16 *>(a.q) + q_row * HD + 8 * part);
 #pragma unroll
-        for (int ds = 0; ds < T::DS; ++ds) {
+        for (int ds = 0; ds < NQF; ++ds) {
             if (row_valid) {
-                st.qf[ds] = qp[2 * ds];
+                st.qf[ds] = qp[(R16 ? 4 : 2) * ds];
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
@@ -627,14 +855,29 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
     // loads is placed before the key loop; inside the loop any vmcnt wait
     // would also wait for the K/V prefetch in flight.
 #pragma unroll
-    for (int ds = 0; ds < T::DS; ++ds)
+    for (int ds = 0; ds < NQF; ++ds)
         asm volatile("" :: "v"(st.qf[ds]));
+    constexpr int NACC = sizeof(st.acc) / sizeof(float);   // accumulator floats per lane
+    auto acc_at = [&](int i) __attribute__((always_inline)) -> float {
+        if constexpr (R16)
+            return st.acc[i / 4][i % 4];
+        else
+            return st.acc[i / 16][i % 16];
+    };
     auto start = [&]() __attribute__((always_inline)) {
+        if constexpr (R16) {
 #pragma unroll
-        for (int db = 0; db < T::DB; ++db)
+            for (int dt = 0; dt < T::DT16; ++dt)
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-                st.acc[db][j] = 0.0f;
+                for (int i = 0; i < 4; ++i)
+                    st.acc[dt][i] = 0.0f;
+        } else {
+#pragma unroll
+            for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    st.acc[db][i] = 0.0f;
+        }
         st.m = -INFINITY;
         st.l = 0.0f;
         wait_loads(kb_pre - kb_begin - 1);
@@ -653,7 +896,7 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
     // barriers; it skips the block computation and leaves its SIMD to the
     // other workgroup on the CU (FP8 decode 14 % faster).  Uniform per wave.
     // (At head_dim 256, one workgroup per CU, the branch only costs spills.)
-    const bool wave_rows = w * 32 < it.n_tok * g;
+    const bool wave_rows = w * T::RPW < it.n_tok * g;
     // Tiles whose first row sees at most kHiLoKeys keys (rows with few keys,
     // where single keys carry much of the softmax) split P on every block.
     // Other final items round P to bf16 and are recomputed with P split on
@@ -681,8 +924,10 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
             }
             const char *Ks = smem + BUF * T::STAGE_BYTES;
             const char *Vs = Ks + T::TILE_BYTES;
-            const int thr = lim_row - kb * T::BK - 4 * h;
-            if (HD != 128 || wave_rows)
+            const int thr = lim_row - kb * T::BK - 4 * part;
+            if constexpr (R16)
+                block_step16<HD, POS_SCALE, MASK, FORCE>(st, Ks, Vs, c, thr, row_valid, trig, kappa, qc, part);
+            else if (HD != 128 || wave_rows)
                 block_step<HD, POS_SCALE, MASK, FORCE>(st, Ks, Vs, c, thr, row_valid, trig, kappa,
                                                        qc, h, grp, s16);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // block kb + 1 has landed
@@ -714,18 +959,16 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
         if (final_item) {
             // Recompute?  A wave votes for it when one of its valid rows has
             // an output element with |O| >= kRecomputeAbsO; the flags of the
-            // four waves are combined through LDS (after the staging area,
+            // waves are combined through LDS (after the staging area,
             // which the epilogue reuses), and the workgroup recomputes
             // together (the K/V staging is shared).
             bool redo = false;
             {
-                const float lt = pair_sum(st.l);
+                const float lt = row_sum<HD>(st.l);
                 float omax = 0.0f;
 #pragma unroll
-                for (int db = 0; db < T::DB; ++db)
-#pragma unroll
-                    for (int j = 0; j < 16; ++j)
-                        omax = fmaxf(omax, fabsf(st.acc[db][j]));
+                for (int i = 0; i < NACC; ++i)
+                    omax = fmaxf(omax, fabsf(acc_at(i)));
                 if (FP8)
                     omax *= fabsf(a.v_scale);
                 redo = row_valid && lt > 0.0f && omax >= kRecomputeAbsO * lt;
@@ -735,8 +978,13 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
             if (lane == 0)
                 flags[w] = wave_redo ? 1 : 0;
             __syncthreads();
-            const int4 f = *reinterpret_cast<const int4 *>(flags);
-            if (f.x | f.y | f.z | f.w) {
+            int any_redo = 0;
+#pragma unroll
+            for (int i = 0; i < T::NW / 4; ++i) {
+                const int4 f = reinterpret_cast<const int4 *>(flags)[i];
+                any_redo |= f.x | f.y | f.z | f.w;
+            }
+            if (any_redo) {
                 first_loads();
                 start();
                 run_forced();
@@ -745,7 +993,7 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
     }
 
     // ---- epilogue ----
-    const float lt = pair_sum(st.l);
+    const float lt = row_sum<HD>(st.l);
     const float inv = lt > 0.0f ? (FP8 ? a.v_scale : 1.0f) / lt : 0.0f;
     const float lse2 = lt > 0.0f ? st.m + log2f(lt) : -INFINITY;
     // The outputs go out through LDS (the K/V stages are free after the last
@@ -756,12 +1004,72 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
     // bytes (the g heads of a token are adjacent rows of O).
     const float inv_g = 1.0f / (float)g;
     auto row_out = [&](int rr, size_t &orow) __attribute__((always_inline)) {
-        const int R = w * 32 + rr;
+        const int R = w * T::RPW + rr;
         const int tk = (int)(((float)R + 0.5f) * inv_g);
         orow = (size_t)(it.q_tok0 + tk) * a.num_qo_heads + it.kv_head * g + (R - tk * g);
         return tk < it.n_tok;
     };
-    if (it.slot < 0) {
+    if (R16 && it.slot < 0) {
+        // 16-row waves: acc[dt][i] is d = 16 dt + 4 part + i of row qc, so a
+        // 16-byte chunk 2 dt + part / 2 is written by lanes part and part ^ 1
+        constexpr int CPR = T::CPR;
+        constexpr int RPI = 64 / CPR;
+        char *wl = smem + w * (T::RPW * T::RB);
+#pragma unroll
+        for (int dt = 0; dt < T::DT16; ++dt) {
+            bf16x4 ov;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ov[e] = (__bf16)(acc_at(4 * dt + e) * inv);
+            const int cc = 2 * dt + (part >> 1);
+            *reinterpret_cast<bf16x4 *>(wl + qc * T::RB + 16 * (cc ^ (qc & (CPR - 1))) + 8 * (part & 1)) = ov;
+        }
+#pragma unroll
+        for (int i = 0; i < T::RPW / RPI; ++i) {
+            const int rr = RPI * i + lane / CPR;
+            const int cc = lane % CPR;
+            const bf16x8 x = *reinterpret_cast<const bf16x8 *>(wl + rr * T::RB + 16 * (cc ^ (rr & (CPR - 1))));
+            size_t orow;
+            if (row_out(rr, orow))
+                *reinterpret_cast<bf16x8 *>(static_cast<__bf16 *>(a.o) + orow * HD + 8 * cc) = x;
+        }
+        if (row_valid && part == 0 && a.lse != nullptr)
+            a.lse[q_row] = lse2 == -INFINITY ? -INFINITY : lse2 * kLn2;
+    } else if (R16) {
+        // fp32 partial state in two passes over d: d tiles 8 pass .. + 7,
+        // chunk 4 (dt - 8 pass) + part of a 512-byte row
+        constexpr int DTP = T::DT16 / 2;
+        constexpr int CPRF = DTP * 4;
+        constexpr int RPIF = 64 / CPRF;
+        char *wl = smem + w * (T::RPW * CPRF * 16);
+        float *pbase = a.part_o + (size_t)it.slot * kTileRows * HD;
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+            for (int dtl = 0; dtl < DTP; ++dtl) {
+                const int dt = pass * DTP + dtl;
+                float4 ov;
+                ov.x = acc_at(4 * dt + 0) * inv;
+                ov.y = acc_at(4 * dt + 1) * inv;
+                ov.z = acc_at(4 * dt + 2) * inv;
+                ov.w = acc_at(4 * dt + 3) * inv;
+                const int cc = 4 * dtl + part;
+                *reinterpret_cast<float4 *>(wl + qc * (CPRF * 16) + 16 * (cc ^ (qc & (CPRF - 1)))) = ov;
+            }
+#pragma unroll
+            for (int i = 0; i < T::RPW / RPIF; ++i) {
+                const int rr = RPIF * i + lane / CPRF;
+                const int cc = lane % CPRF;
+                const float4 x = *reinterpret_cast<const float4 *>(
+                    wl + rr * (CPRF * 16) + 16 * (cc ^ (rr & (CPRF - 1))));
+                size_t orow;
+                if (row_out(rr, orow))
+                    *reinterpret_cast<float4 *>(pbase + (size_t)(w * T::RPW + rr) * HD + pass * DTP * 16 + 4 * cc) = x;
+            }
+        }
+        if (row_valid && part == 0)
+            a.part_lse[(size_t)it.slot * kTileRows + r] = lse2;
+    } else if (it.slot < 0) {
         constexpr int CPR = T::CPR;          // 16-byte chunks per bf16 row
         constexpr int RPI = 64 / CPR;        // rows per read instruction
         char *wl = smem + w * (32 * T::RB);
@@ -826,7 +1134,7 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
 }
 
 template <int HD, bool PAGED, bool FP8>
-__global__ __launch_bounds__(kThreads, HD == 128 ? 2 : 1) void tile_kernel(TileArgs a)
+__global__ __launch_bounds__(Tile<HD>::THREADS, HD == 128 ? 2 : 1) void tile_kernel(TileArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const Item it = a.items[blockIdx.x];
@@ -839,9 +1147,9 @@ __global__ __launch_bounds__(kThreads, HD == 128 ? 2 : 1) void tile_kernel(TileA
 }
 
 // dynamic LDS of a tile kernel instance: the K/V stages, the fp8 staging
-// slots, and the four per-wave recompute flags
+// slots, and the per-wave recompute flags
 template <int HD, bool FP8>
-constexpr int tile_lds_bytes() { return Tile<HD>::LDS_BYTES + (FP8 ? 2 * Tile<HD>::BK * HD : 0) + 16; }
+constexpr int tile_lds_bytes() { return Tile<HD>::LDS_BYTES + (FP8 ? 2 * Tile<HD>::BK * HD : 0) + 4 * Tile<HD>::NW; }
 
 template <int HD>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a)
@@ -902,7 +1210,7 @@ int launch_tile(const TileArgs &args, int64_t num_items, hipStream_t stream)
         attr_devices.fetch_or(bit, std::memory_order_release);
     }
     auto kernel = tile_kernel<HD, PAGED, FP8>;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)num_items), dim3(kThreads), lds, stream, args);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)num_items), dim3(Tile<HD>::THREADS), lds, stream, args);
     return (int)hipGetLastError();
 }
 
