@@ -133,8 +133,8 @@ typedef struct rp_plan_opts {
     int split_mode;  /* enum rp_split_mode */
     int host_only;   /* nonzero: plan on the host only; such a plan can be inspected, not run */
     int num_xcds;    /* XCDs the launch order is arranged for (workgroup b runs on XCD
-                        b % num_xcds); 0 = default (8, the MI355X XCD count, for
-                        head_dim 128; 1 for head_dim 256), 1 = plain longest-first order */
+                        b % num_xcds); 0 = default (8, the MI355X XCD count),
+                        1 = plain longest-first order */
 } rp_plan_opts;
 
 /* Summary of a plan (host side). */

@@ -33,7 +33,7 @@ def _check_plan(qo_lens, kv_lens, hq, hkv, d, causal, kv_chunk=0, q_base=0, kv_b
     p = vp.Plan(qi, ki, hq, hkv, d, causal, kv_chunk=kv_chunk, host_only=True, num_xcds=num_xcds)
     info = p.info
     launch = p.items()
-    xcds = num_xcds or (8 if d == 128 else 1)
+    xcds = num_xcds or 8
     # longest-first within each XCD's share of the launch order (workgroup b
     # runs on XCD b % xcds); padding items (n_tok = 0) carry no work
     for x in range(xcds):
