@@ -233,3 +233,37 @@ def test_16_row_epilogue_lds_writes_are_bank_conflict_free():
             cc = 4 * dtl + part
             addrs.append(n16 * cpr * 16 + 16 * (cc ^ (n16 & (cpr - 1))))
         assert _cycles(addrs, 16, 16) == 0, dtl
+
+
+def test_32_row_epilogue_lds_writes_are_bank_conflict_free():
+    """head_dim 128: after the permlane32 swap the lower lane of a row writes
+    chunk 4 db + 2 p and the upper lane chunk 4 db + 2 p + 1 (16 bytes each);
+    the fp32 partial-state writes are 16-byte chunks 8 dbl + 2 jj + h"""
+    hd = 128
+    rb, cpr = hd * 2, hd // 8
+    for db in range(hd // 32):
+        for p in range(2):
+            addrs = []
+            for lane in range(64):
+                h, qc = lane >> 5, lane & 31
+                cc = 4 * db + 2 * p + h
+                addrs.append(qc * rb + 16 * (cc ^ (qc & (cpr - 1))))
+            assert _cycles(addrs, 16, 16) == 0, (db, p)
+    # every 16-byte chunk of the wave's 32 rows is written exactly once
+    seen = set()
+    for lane in range(64):
+        h, qc = lane >> 5, lane & 31
+        for db in range(hd // 32):
+            for p in range(2):
+                cc = 4 * db + 2 * p + h
+                seen.add((qc, cc ^ (qc & (cpr - 1))))
+    assert len(seen) == 32 * cpr
+    cprf = hd // 32 // 2 * 8
+    for dbl in range(hd // 64):
+        for jj in range(4):
+            addrs = []
+            for lane in range(64):
+                h, qc = lane >> 5, lane & 31
+                cc = 8 * dbl + 2 * jj + h
+                addrs.append(qc * cprf * 16 + 16 * (cc ^ (qc & (cprf - 1))))
+            assert _cycles(addrs, 16, 16) == 0, (dbl, jj)

@@ -1073,16 +1073,33 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
         constexpr int CPR = T::CPR;          // 16-byte chunks per bf16 row
         constexpr int RPI = 64 / CPR;        // rows per read instruction
         char *wl = smem + w * (32 * T::RB);
+        // Lane half h holds bytes 8 h .. 8 h + 7 of every 16-byte chunk of its
+        // row; one permlane32 swap per dword pairs the halves, so that the
+        // lower lane writes chunk 4 db + 2 p and the upper lane chunk
+        // 4 db + 2 p + 1 whole (16-byte writes, no bank conflicts).
+        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
         for (int db = 0; db < T::DB; ++db)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                bf16x4 ov;
+            for (int pp = 0; pp < 2; ++pp) {
+                bf16x4 ox, oy;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    ov[e] = (__bf16)(st.acc[db][4 * jj + e] * inv);
-                const int cc = 4 * db + jj;
-                *reinterpret_cast<bf16x4 *>(wl + qc * T::RB + 16 * (cc ^ (qc & (CPR - 1))) + 8 * h) = ov;
+                for (int e = 0; e < 4; ++e) {
+                    ox[e] = (__bf16)(st.acc[db][8 * pp + e] * inv);
+                    oy[e] = (__bf16)(st.acc[db][8 * pp + 4 + e] * inv);
+                }
+                const u32x2 x2 = __builtin_bit_cast(u32x2, ox);
+                const u32x2 y2 = __builtin_bit_cast(u32x2, oy);
+                auto r0 = __builtin_amdgcn_permlane32_swap(x2[0], y2[0], false, false);
+                auto r1 = __builtin_amdgcn_permlane32_swap(x2[1], y2[1], false, false);
+                u32x4 ch;
+                ch[0] = r0[0];
+                ch[1] = r1[0];
+                ch[2] = r0[1];
+                ch[3] = r1[1];
+                const int cc = 4 * db + 2 * pp + h;
+                *reinterpret_cast<u32x4 *>(wl + qc * T::RB + 16 * (cc ^ (qc & (CPR - 1)))) = ch;
             }
 #pragma unroll
         for (int i = 0; i < 32 / RPI; ++i) {
