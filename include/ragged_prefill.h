@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define RP_ABI_VERSION 6
+#define RP_ABI_VERSION 7
 
 /* Status codes. */
 enum rp_status {
@@ -119,10 +119,19 @@ int ragged_prefill_bf16(const void *q, const void *k, const void *v, void *o, fl
 
 typedef struct rp_plan rp_plan;
 
+/* Placement of tiles whose visible keys span more than one canonical KV
+ * chunk.  Either way each chunk's state is computed from a fresh start and
+ * the states are folded in ascending chunk order with the same arithmetic
+ * (merge of attention states, page "flashinfer-ai/flashinfer", "Merge
+ * Attention States"; split-KV scheduled automatically, same page, attention
+ * API, task-scheduled attention), so the three modes give identical bits. */
 enum rp_split_mode {
-    RP_SPLIT_AUTO = 0,    /* split every tile whose visible keys span more than one KV chunk */
+    RP_SPLIT_AUTO = 0,    /* NEVER at head_dim 128 when the longest folded tile costs no more
+                             than the average load of the 512 workgroups resident on the GPU
+                             (the grid fills it without split-KV); ALWAYS otherwise */
+    RP_SPLIT_NEVER = 1,   /* one workgroup per tile runs its chunks in order and folds their
+                             states itself (running state in a workspace slot, no merge kernel) */
     RP_SPLIT_ALWAYS = 2   /* one workgroup per (tile, KV chunk) + merge kernel */
-    /* 1 is reserved (rp_plan_create returns RP_EINVAL for it) */
 };
 
 /* Planner options.  All-zero means defaults.  The KV chunk size fixes the
@@ -151,6 +160,7 @@ typedef struct rp_plan_info {
     double flops;              /* algorithmic: 4 * head_dim * num_qo_heads * visible pairs */
     double bytes;              /* algorithmic: Q,K,V read once, O,LSE written once */
     size_t workspace_bytes;    /* bytes rp_run needs (0 if no partial states) */
+    int64_t num_fold_items;    /* of num_items, those that fold their tile's KV chunks */
 } rp_plan_info;
 
 /* Build a plan from HOST offsets.  On success *out owns a plan (possibly with

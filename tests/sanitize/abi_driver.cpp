@@ -94,7 +94,8 @@ void run_batch(const Batch &b, int iter)
     static const int chunks[] = {0, 64, 128, 192, 1024};
     rp_plan_opts opts{};
     opts.kv_chunk = chunks[rnd() % 5];
-    opts.split_mode = rnd() % 2 ? RP_SPLIT_AUTO : RP_SPLIT_ALWAYS;
+    static const int modes[] = {RP_SPLIT_AUTO, RP_SPLIT_NEVER, RP_SPLIT_ALWAYS};
+    opts.split_mode = modes[rnd() % 3];
     opts.num_xcds = (int)(rnd() % 9);
     rp_plan *plan = nullptr;
     int st = rp_plan_create(b.qi.data(), b.ki.data(), b.batch, b.hq, b.hkv, b.d, b.causal, &opts, &plan);
@@ -206,8 +207,8 @@ void invalid_inputs(int iter)
     expect(rp_plan_create(ok, ok, 2, 8, 3, 128, 1, nullptr, &p) == RP_EINVAL, "heads not a multiple", iter);
     expect(rp_plan_create(ok, ok, 2, 8, 2, 96, 1, nullptr, &p) == RP_EUNSUPPORTED, "head_dim 96", iter);
     rp_plan_opts o{};
-    o.split_mode = 1;
-    expect(rp_plan_create(ok, ok, 2, 8, 2, 128, 1, &o, &p) == RP_EINVAL, "split mode 1", iter);
+    o.split_mode = 3;
+    expect(rp_plan_create(ok, ok, 2, 8, 2, 128, 1, &o, &p) == RP_EINVAL, "split mode 3", iter);
     o.split_mode = 0;
     o.kv_chunk = 100;
     expect(rp_plan_create(ok, ok, 2, 8, 2, 128, 1, &o, &p) == RP_EINVAL, "kv_chunk 100", iter);

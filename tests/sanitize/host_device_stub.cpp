@@ -92,8 +92,13 @@ hipError_t hipGetDevicePropertiesR0600(hipDeviceProp_tR0600 *, int) { return hip
 
 namespace rp {
 
-int launch_tile_kernel(int head_dim, bool paged, bool fp8, const TileArgs &a, int64_t num_items,
-                       void *)
+int launch_tile_fold_kernel(int, bool, bool, const TileArgs &, int64_t, void *)
+{
+    contract("fold launcher called directly", 0, 0);
+}
+
+int launch_tile_kernel(int head_dim, bool paged, bool fp8, bool fold, const TileArgs &a,
+                       int64_t num_items, void *)
 {
     const int g = a.group;
     const size_t elem = fp8 ? 1 : 2;   // K/V bytes per element
@@ -107,6 +112,10 @@ int launch_tile_kernel(int head_dim, bool paged, bool fp8, const TileArgs &a, in
             contract("tile token range", it.t0, it.n_tok);
         if (it.kv_head < 0 || it.kv_head >= a.num_kv_heads)
             contract("kv head", it.kv_head, a.num_kv_heads);
+        // a fold item writes the final O/LSE and keeps its running state in its slot
+        const bool fold_item = it.fold_keys > 0;
+        if (fold_item && (!fold || it.slot < 0))
+            contract("fold item in a launch without fold items", it.slot, fold ? 1 : 0);
         const bool keys = it.key_end > it.key_begin;
         if (keys && (it.key_begin < 0 || it.key_end > it.kv_len))
             contract("key range", it.key_begin, it.key_end);
@@ -115,7 +124,7 @@ int launch_tile_kernel(int head_dim, bool paged, bool fp8, const TileArgs &a, in
             const size_t row = (size_t)it.q_tok0 + t;
             const size_t off = row * q_row + (size_t)it.kv_head * g * head_dim * 2;
             touch_read(static_cast<const char *>(a.q) + off, (size_t)g * head_dim * 2);
-            if (it.slot < 0) {
+            if (it.slot < 0 || fold_item) {
                 touch_write(static_cast<char *>(a.o) + off, (size_t)g * head_dim * 2);
                 if (a.lse)
                     touch_write(a.lse + row * a.num_qo_heads + (size_t)it.kv_head * g, (size_t)g * 4);

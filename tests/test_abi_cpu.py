@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = _lib.load()
-    assert lib.rp_abi_version() == 6
+    assert lib.rp_abi_version() == 7
     for st in (0, -1, -2, -3, -4):
         assert lib.rp_status_string(st)
     assert lib.rp_status_string(12345) == b"unknown status"
@@ -70,7 +70,7 @@ def _plan(qi, ki, hq=8, hkv=2, d=128, causal=True, **kw):
     (dict(hq=256, hkv=1), _lib.RP_EUNSUPPORTED),      # group above 128
     (dict(kv_chunk=100), _lib.RP_EINVAL),             # chunk not a multiple of 64
     (dict(split_mode=7), _lib.RP_EINVAL),
-    (dict(split_mode=1), _lib.RP_EINVAL),
+    (dict(split_mode=-1), _lib.RP_EINVAL),
 ])
 def test_plan_validation(kwargs, status):
     with pytest.raises(vp.RaggedPrefillError) as ei:

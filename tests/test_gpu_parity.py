@@ -97,11 +97,21 @@ def test_small_ragged(case):
 
 
 @pytest.mark.parametrize("d", [128, 256])
-def test_split_kv_chunks(d):
-    # a small canonical chunk forces split tiles + the merge kernel
+@pytest.mark.parametrize("mode", ["always", "never"])
+def test_split_kv_chunks(d, mode):
+    # a small canonical chunk makes multi-chunk tiles: split items + the merge
+    # kernel ("always") or items that fold their chunks in the workgroup ("never")
+    import varlen_prefill_amd as vp
+    split_mode = vp.RP_SPLIT_ALWAYS if mode == "always" else vp.RP_SPLIT_NEVER
     b = make_batch([50, 300, 9], [700, 300, 1000], 8, 2, d, seed=2000 + d)
     for causal in (True, False):
-        _check_full(b, causal, default_scale(d), kv_chunk=128)
+        _check_full(b, causal, default_scale(d), kv_chunk=128, split_mode=split_mode)
+    # non-positive scales take the other kernel branch
+    for sm in (0.0, -0.05):
+        o, lse = _gpu(b, True, sm, kv_chunk=128, split_mode=split_mode)
+        ro, rl = _oracle(b, True, sm)
+        rows = _rows_in_requests(b)
+        compare(bf16_to_f64(o)[rows], lse.double().numpy()[rows], ro[rows], rl[rows])
 
 
 def _run_variant(batch, variant, **plan_kw):
@@ -163,6 +173,26 @@ def test_split_mode_always_matches_auto_bitwise():
     so, sl = _gpu(b, True, default_scale(128), kv_chunk=1024, split_mode=vp.RP_SPLIT_ALWAYS)
     assert torch.equal(ao.view(torch.int16), so.view(torch.int16))
     assert torch.equal(al.view(torch.int32), sl.view(torch.int32))
+
+
+@pytest.mark.parametrize("d,variant", [(128, "bf16"), (256, "bf16"), (128, "fp8"), (256, "fp8"),
+                                       (128, "paged"), (256, "paged")])
+def test_split_modes_bitwise(d, variant):
+    """In-workgroup chunk folding (NEVER), split items + merge kernel
+    (ALWAYS) and the automatic choice give the same bits, for every kernel
+    instance; the canonical chunk of 192 keys gives tiles of 2..11 chunks,
+    a ragged last chunk, and chunks a tile's causal rows only partly see."""
+    import varlen_prefill_amd as vp
+    qo, kv = [50, 300, 9, 1, 130, 64], [700, 300, 1000, 2100, 2000, 64]
+    b = make_batch(qo, kv, 8, 2, d, seed=3000 + d)
+    info = vp.Plan(b.q_indptr, b.kv_indptr, 8, 2, d, True, kv_chunk=192,
+                   split_mode=vp.RP_SPLIT_NEVER, host_only=True).info
+    assert info["num_fold_items"] > 0 and info["num_merge_items"] == 0
+    ref_o, ref_l = _run_variant(b, variant, kv_chunk=192, split_mode=vp.RP_SPLIT_ALWAYS)
+    for mode in (vp.RP_SPLIT_NEVER, vp.RP_SPLIT_AUTO):
+        o, l = _run_variant(b, variant, kv_chunk=192, split_mode=mode)
+        assert torch.equal(o.view(torch.int16), ref_o.view(torch.int16)), mode
+        assert torch.equal(l.view(torch.int32), ref_l.view(torch.int32)), mode
 
 
 def test_repeat_runs_bitwise():
@@ -418,7 +448,7 @@ def _scale_keys(batch, factor):
 
 
 STRESS = ["growing", "sink", "wide_scale", "growing_split", "growing_hd256", "sink_hd256",
-          "wide_scale_hd256", "wide_scale_split"]
+          "wide_scale_hd256", "wide_scale_split", "growing_fold", "wide_scale_fold"]
 
 
 @pytest.mark.parametrize("mode", STRESS)
@@ -444,4 +474,7 @@ def test_reference_max_moves(mode):
         sm = 1.0
     if mode.endswith("_split"):
         plan_kw["kv_chunk"] = 128
+    if mode.endswith("_fold"):
+        import varlen_prefill_amd as vp
+        plan_kw.update(kv_chunk=128, split_mode=vp.RP_SPLIT_NEVER)
     _check_full(b, True, sm, **plan_kw)

@@ -26,7 +26,7 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 from . import _lib
-from ._lib import (RP_SPLIT_ALWAYS, RP_SPLIT_AUTO, RaggedPrefillError,
+from ._lib import (RP_SPLIT_ALWAYS, RP_SPLIT_AUTO, RP_SPLIT_NEVER, RaggedPrefillError,
                    RpPlanInfo, RpPlanOpts)
 
 __all__ = [
@@ -39,13 +39,14 @@ __all__ = [
     "merge_states",
     "RaggedPrefillError",
     "RP_SPLIT_AUTO",
+    "RP_SPLIT_NEVER",
     "RP_SPLIT_ALWAYS",
     "ITEM_FIELDS",
 ]
 
 # field names of one worklist item (int32 x 16), see rp_internal.h
 ITEM_FIELDS = ["q_tok0", "n_tok", "t0", "qo_len", "kv_row0", "kv_len", "kv_head", "key_begin",
-               "key_end", "slot", "request", "chunk", "cost", "lim_first", "reserved0",
+               "key_end", "slot", "request", "chunk", "cost", "lim_first", "fold_keys",
                "reserved1"]
 
 

@@ -22,6 +22,7 @@ RP_ENOMEM = -3
 RP_EDEVICE = -4
 
 RP_SPLIT_AUTO = 0
+RP_SPLIT_NEVER = 1
 RP_SPLIT_ALWAYS = 2
 
 RP_ITEM_INTS = 16
@@ -63,7 +64,8 @@ class RpPlanInfo(ctypes.Structure):
                 ("total_kv", ctypes.c_int64), ("tile_rows", ctypes.c_int32),
                 ("tile_tokens", ctypes.c_int32), ("key_block", ctypes.c_int32),
                 ("kv_chunk", ctypes.c_int32), ("flops", ctypes.c_double),
-                ("bytes", ctypes.c_double), ("workspace_bytes", ctypes.c_size_t)]
+                ("bytes", ctypes.c_double), ("workspace_bytes", ctypes.c_size_t),
+                ("num_fold_items", ctypes.c_int64)]
 
 
 class RaggedPrefillError(RuntimeError):

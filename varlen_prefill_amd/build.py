@@ -18,7 +18,17 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(BUILD, "librp.so")
 INCLUDE = os.path.join(ROOT, "include")
 
-SOURCES = ["rp_kernels.hip", "rp_state_merge.hip", "rp_noalloc.hip", "rp_plan.cpp", "rp_api.cpp"]
+# (source, object, extra flags): the tile kernel source is built twice, once
+# for the plain tile kernels and once for the instances that also run fold
+# items (in-workgroup chunk folding)
+SOURCES = [
+    ("rp_kernels.hip", "rp_kernels.o", []),
+    ("rp_kernels.hip", "rp_kernels_fold.o", ["-DRP_TILE_FOLD=1"]),
+    ("rp_state_merge.hip", "rp_state_merge.o", []),
+    ("rp_noalloc.hip", "rp_noalloc.o", []),
+    ("rp_plan.cpp", "rp_plan.o", []),
+    ("rp_api.cpp", "rp_api.o", []),
+]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -40,19 +50,27 @@ def hipcc() -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    objs = []
-    for src in SOURCES:
+    objs, procs = [], []
+    # the objects compile in parallel (the two tile-kernel objects dominate)
+    for src, obj_name, extra in SOURCES:
         path = os.path.join(CSRC, src)
-        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(BUILD, obj_name)
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE, "-I", CSRC] + lang + ["-c", path, "-o", obj]
+        cmd = ([hipcc()] + HIPCC_FLAGS + extra + ["-I", INCLUDE, "-I", CSRC] + lang +
+               ["-c", path, "-o", obj])
         if verbose:
             print(" ".join(cmd))
-        res = subprocess.run(cmd, capture_output=True, text=True)
-        if res.returncode != 0:
-            sys.stderr.write(res.stdout + res.stderr)
-            raise RuntimeError(f"hipcc failed on {src}")
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                            text=True)))
         objs.append(obj)
+    failed = []
+    for src, proc in procs:
+        out, _ = proc.communicate()
+        if proc.returncode != 0:
+            sys.stderr.write(out)
+            failed.append(src)
+    if failed:
+        raise RuntimeError(f"hipcc failed on {', '.join(failed)}")
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)

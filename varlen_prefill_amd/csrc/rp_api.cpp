@@ -179,10 +179,10 @@ int create_plan(const int32_t *q_indptr, const int32_t *kv_indptr, int batch, in
         }
     }
     logf(1, "plan: batch=%d Hq=%d Hkv=%d D=%d causal=%d total_q=%lld total_kv=%lld items=%zu "
-            "partial=%lld merges=%zu kv_chunk=%d gflop=%.3f mb=%.3f",
+            "partial=%lld fold=%lld merges=%zu kv_chunk=%d gflop=%.3f mb=%.3f",
          batch, num_qo_heads, num_kv_heads, head_dim, causal, (long long)p->host.total_q,
          (long long)p->host.total_kv, p->host.items.size(), (long long)p->host.num_partial_items,
-         p->host.merges.size(), p->host.shape.kv_chunk, p->host.flops * 1e-9, p->host.bytes * 1e-6);
+         (long long)p->host.num_fold_items, p->host.merges.size(), p->host.shape.kv_chunk, p->host.flops * 1e-9, p->host.bytes * 1e-6);
     *out = p;
     return RP_OK;
 }
@@ -335,8 +335,8 @@ int run_plan(const rp_plan *p, const void *q, const void *k, const void *v, void
     }
     logf(3, "launch tile kernel: D=%d items=%zu merges=%zu scale_log2=%g", h.shape.head_dim,
          h.items.size(), h.merges.size(), (double)ta.scale_log2);
-    int st = rp::launch_tile_kernel(h.shape.head_dim, paged != nullptr, fp8 != nullptr, ta,
-                                    (int64_t)h.items.size(), stream);
+    int st = rp::launch_tile_kernel(h.shape.head_dim, paged != nullptr, fp8 != nullptr,
+                                    h.num_fold_items > 0, ta, (int64_t)h.items.size(), stream);
     if (st != (int)hipSuccess)
         return hip_fail((hipError_t)st, "tile kernel launch");
     if (!h.merges.empty()) {
@@ -449,6 +449,7 @@ int rp_plan_get_info(const rp_plan *p, rp_plan_info *info)
     info->num_items = (int64_t)h.items.size();
     info->num_partial_items = h.num_partial_items;
     info->num_merge_items = (int64_t)h.merges.size();
+    info->num_fold_items = h.num_fold_items;
     info->total_q = h.total_q;
     info->total_kv = h.total_kv;
     info->tile_rows = rp::kTileRows;
@@ -463,6 +464,7 @@ int rp_plan_get_info(const rp_plan *p, rp_plan_info *info)
         info->num_items += (int64_t)s.items.size();
         info->num_partial_items += s.num_partial_items;
         info->num_merge_items += (int64_t)s.merges.size();
+        info->num_fold_items += s.num_fold_items;
         info->total_kv += s.total_kv;
         info->flops += s.flops;
         info->bytes += 2.0 * 2.0 * (double)s.total_kv * h.shape.num_kv_heads * h.shape.head_dim;

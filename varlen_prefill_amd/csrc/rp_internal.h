@@ -31,6 +31,11 @@ constexpr int kChunkAlign = 64;     // kv_chunk must be a multiple of this
 constexpr int kDecodeRows = 32;
 constexpr int kDecodeChunk = 2048;
 constexpr int kDefaultXcds = 8;     // MI355X: 8 XCDs, workgroups dispatched round-robin
+// Workgroups of the head_dim 128 tile kernel resident at once on an MI355X
+// (256 CUs x 2).  The automatic split mode folds a tile's KV chunks in one
+// workgroup when the longest folded tile costs no more than the work each of
+// these would get on average: the grid then fills the GPU without split-KV.
+constexpr int kResidentTiles128 = 512;
 // P enters the PV product either rounded to bf16 or split into a bf16 hi part
 // and a bf16 lo remainder (two MFMAs, accurate to about 2^-17).
 //
@@ -85,12 +90,13 @@ struct Item {
     int32_t kv_head;    // kv head; qo heads kv_head*g .. kv_head*g+g-1
     int32_t key_begin;  // request-relative first key of this item
     int32_t key_end;    // request-relative end key (exclusive); <= key_begin: no keys
-    int32_t slot;       // -1: write final O/LSE; >= 0: partial-state slot
+    int32_t slot;       // -1: write final O/LSE; >= 0: partial-state slot (a fold item's running state)
     int32_t request;    // request index in the batch
     int32_t chunk;      // canonical chunk index of a partial item; chunk count otherwise
     int32_t cost;       // planner's cost estimate (key blocks, hi/lo weighted)
     int32_t lim_first;  // keys visible to the tile's first row (causal limit)
-    int32_t reserved0;
+    int32_t fold_keys;  // > 0: the workgroup folds the tile's KV chunks of this many keys
+                        // itself (running state in slot `slot`, final O/LSE written)
     int32_t reserved1;
 };
 static_assert(sizeof(Item) == 64, "Item must stay 16 int32");
@@ -145,8 +151,11 @@ struct MergeArgs {
 };
 
 // Host-side launchers (defined in the .hip file).  Return a hipError_t value.
-int launch_tile_kernel(int head_dim, bool paged, bool fp8, const TileArgs &args, int64_t num_items,
-                       void *stream);
+// fold: the plan has fold items (launches the instance that runs them)
+int launch_tile_kernel(int head_dim, bool paged, bool fp8, bool fold, const TileArgs &args,
+                       int64_t num_items, void *stream);
+int launch_tile_fold_kernel(int head_dim, bool paged, bool fp8, const TileArgs &args, int64_t num_items,
+                            void *stream);
 int launch_merge_kernel(int head_dim, const MergeArgs &args, int64_t num_items, void *stream);
 
 }  // namespace rp

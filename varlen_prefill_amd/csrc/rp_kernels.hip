@@ -32,6 +32,14 @@
 // in ascending key order (merge of attention states, page
 // "flashinfer-ai/flashinfer", "Merge Attention States"), and writes bf16 O
 // and the natural-log LSE.
+//
+// Fold items (in-workgroup chunk folding): one workgroup runs all canonical
+// KV chunks of a tile in order, each from a fresh state by the rules of a
+// split item, and folds each chunk's normalised state into a running state
+// in its workspace slot with the merge kernel's arithmetic and order, then
+// writes O and LSE itself: the same bits as split items + merge kernel,
+// without the merge launch and with one partial-state slot per tile instead
+// of one per chunk.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -40,6 +48,13 @@
 #include <type_traits>
 
 #include "rp_internal.h"
+
+// Built twice: RP_TILE_FOLD 0 gives the plain tile kernels, the merge kernel
+// and the launchers; RP_TILE_FOLD 1 the tile kernels that also run fold
+// items (in-workgroup chunk folding) and their launcher.
+#ifndef RP_TILE_FOLD
+#define RP_TILE_FOLD 0
+#endif
 
 namespace rp {
 namespace {
@@ -145,26 +160,36 @@ __device__ inline float row_sum(float x) { return Tile<HD>::RPW == 32 ? pair_sum
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Fold state b into state a (base-2 log-sum-exp, normalised outputs):
+// Fold of state b into state a (base-2 log-sum-exp, normalised outputs):
 //   lse = log2(2^lse_a + 2^lse_b),  o = o_a 2^(lse_a - lse) + o_b 2^(lse_b - lse).
-// Written without fma contraction so that every caller rounds identically.
-template <int N>
-__device__ inline void fold_state(float &lse_a, float (&o_a)[N], float lse_b, const float (&o_b)[N])
+// Written without fma contraction so that every caller (the merge kernel and
+// the tile kernel's in-workgroup fold) rounds identically.  keep: both states
+// are empty (lse -inf), a stays as it is.
+struct FoldWeights {
+    float ca, cb, lse;
+    bool keep;
+};
+
+__device__ inline FoldWeights fold_weights(float lse_a, float lse_b)
 {
 #pragma clang fp contract(off)
+    FoldWeights f;
     const float mx = fmaxf(lse_a, lse_b);
-    if (mx == -INFINITY)
-        return;
+    f.keep = mx == -INFINITY;
     const float wa = fast_exp2(lse_a - mx);
     const float wb = fast_exp2(lse_b - mx);
     const float s = wa + wb;
     const float inv = 1.0f / s;
-    const float ca = wa * inv;
-    const float cb = wb * inv;
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-        o_a[i] = o_a[i] * ca + o_b[i] * cb;
-    lse_a = mx + log2f(s);
+    f.ca = wa * inv;
+    f.cb = wb * inv;
+    f.lse = f.keep ? lse_a : mx + log2f(s);
+    return f;
+}
+
+__device__ inline float fold_value(const FoldWeights &f, float o_a, float o_b)
+{
+#pragma clang fp contract(off)
+    return f.keep ? o_a : o_a * f.ca + o_b * f.cb;
 }
 
 // Registers one wave carries through a tile.
@@ -599,12 +624,16 @@ __device__ __attribute__((always_inline)) inline void block_step16(
     }
 }
 
-template <int HD, bool POS_SCALE, bool PAGED, bool FP8>
-__device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
+template <int HD, bool POS_SCALE, bool PAGED, bool FP8, bool FOLD>
+__device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem, int fc)
 {
     using T = Tile<HD>;
     constexpr bool R16 = T::RPW == 16;
-    const int tid = threadIdx.x;
+    int tid = threadIdx.x;
+    // (the lane values of chunk fc are recomputed from an opaque thread id:
+    // hoisted out of the chunk loop they would stay live across it)
+    if constexpr (FOLD)
+        asm volatile("" : "+v"(tid));
     const int lane = tid & 63;
     const int w = tid >> 6;
     const int qc = lane & (T::RPW - 1);   // the lane's row within the wave (MFMA column)
@@ -628,8 +657,12 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
     }
 
     const float c = a.scale_log2;
-    const int kb_begin = it.key_begin / T::BK;
-    const int kb_end = it.key_end > it.key_begin ? (it.key_end + T::BK - 1) / T::BK : kb_begin;
+    // FOLD: this call runs canonical KV chunk fc of a fold item (fold_keys
+    // keys per chunk) from a fresh state, by the rules of a split item.
+    const int chunk_begin = FOLD ? it.key_begin + fc * it.fold_keys : it.key_begin;
+    const int chunk_end = FOLD ? min(it.key_end, chunk_begin + it.fold_keys) : it.key_end;
+    const int kb_begin = chunk_begin / T::BK;
+    const int kb_end = chunk_end > chunk_begin ? (chunk_end + T::BK - 1) / T::BK : kb_begin;
 
     const size_t head_off = ((size_t)(PAGED ? 0 : it.kv_row0) * a.num_kv_heads + it.kv_head) * HD;
     const __bf16 *kbase = static_cast<const __bf16 *>(a.k) + head_off;
@@ -903,7 +936,13 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
     // every block when the result holds an element with |O| >=
     // kRecomputeAbsO (below); partial states of split-KV tiles cannot be
     // recomputed later, so they split P per block by the running-sum test.
-    const bool final_item = it.slot < 0;
+    // Fold items follow the rules of split items (slot >= 0).  Their slot is
+    // made opaque so that the key loop is compiled as for any item (known
+    // at compile time, the specialised loop needs more registers at head_dim 256).
+    int slot_rt = it.slot;
+    if constexpr (FOLD)
+        asm volatile("" : "+s"(slot_rt));
+    const bool final_item = slot_rt < 0;
     const bool force = it.lim_first <= kHiLoKeys;
     const bool trig = !final_item;
     const float kappa = trig ? kHiLoFracPartial / (1.0f - kHiLoFracPartial) : INFINITY;
@@ -951,6 +990,61 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
         run(std::false_type{}, std::true_type{}, kb_begin, kb_mask);
         run(std::true_type{}, std::true_type{}, kb_mask, kb_end);
     };
+    auto set_acc = [&](int i, float x) __attribute__((always_inline)) {
+        if constexpr (R16)
+            st.acc[i / 4][i % 4] = x;
+        else
+            st.acc[i / 16][i % 16] = x;
+    };
+    // Fold items, at the end of chunk fc: the chunk's normalised state (as a
+    // split item writes it) becomes the running state (first chunk) or is
+    // folded into it.  The running state lives in the item's slot: outputs
+    // in part_o, each lane reading back only what it wrote itself, and the
+    // log-sum-exp in part_lse, written by every lane of the row (the same
+    // value).  After the last chunk the folded outputs replace the
+    // accumulators and the folded log-sum-exp is returned.  Lane layout:
+    // 4 consecutive floats of row r per group of 4 accumulators.
+    constexpr int FOLD_LOADS = 4;
+    auto fold_chunk = [&](bool first, auto last_tag) __attribute__((always_inline)) {
+        constexpr bool LAST = decltype(last_tag)::value;
+        const float lt = row_sum<HD>(st.l);
+        const float inv = lt > 0.0f ? (FP8 ? a.v_scale : 1.0f) / lt : 0.0f;
+        const float lse_c = lt > 0.0f ? st.m + log2f(lt) : -INFINITY;
+        float *orow = a.part_o + ((size_t)it.slot * kTileRows + r) * HD;
+        float *lrow = a.part_lse + (size_t)it.slot * kTileRows + r;
+        const float lse_run = first ? -INFINITY : *lrow;
+        const FoldWeights fw = fold_weights(lse_run, lse_c);
+#pragma unroll
+        for (int gq = 0; gq < NACC / 4; ++gq) {
+            const int d0 = R16 ? 16 * gq + 4 * part : 32 * (gq / 4) + 8 * (gq % 4) + 4 * h;
+            float4 *p4 = reinterpret_cast<float4 *>(orow + d0);
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                o[e] = acc_at(4 * gq + e) * inv;
+            if (!first) {
+                const float4 x = *p4;
+                o[0] = fold_value(fw, x.x, o[0]);
+                o[1] = fold_value(fw, x.y, o[1]);
+                o[2] = fold_value(fw, x.z, o[2]);
+                o[3] = fold_value(fw, x.w, o[3]);
+            }
+            if constexpr (LAST) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    set_acc(4 * gq + e, o[e]);
+            } else {
+                *p4 = make_float4(o[0], o[1], o[2], o[3]);
+            }
+            // at most FOLD_LOADS float4 loads in flight
+            if (gq % FOLD_LOADS == FOLD_LOADS - 1)
+                asm volatile("" ::: "memory");
+        }
+        const float lse_new = first ? lse_c : fw.lse;
+        if (!LAST)
+            *lrow = lse_new;
+        return lse_new;
+    };
     if (force) {
         run_forced();
     } else {
@@ -991,11 +1085,22 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
             }
         }
     }
+    float lse_fold = 0.0f;
+    if constexpr (FOLD) {
+        // the last block's barrier has freed the stages for the next chunk
+        if (chunk_end < it.key_end) {
+            fold_chunk(fc == 0, std::false_type{});
+            return;
+        }
+        lse_fold = fold_chunk(fc == 0, std::true_type{});
+    }
 
     // ---- epilogue ----
     const float lt = row_sum<HD>(st.l);
-    const float inv = lt > 0.0f ? (FP8 ? a.v_scale : 1.0f) / lt : 0.0f;
-    const float lse2 = lt > 0.0f ? st.m + log2f(lt) : -INFINITY;
+    // fold items hold the folded (already normalised) outputs
+    const float inv = FOLD ? 1.0f : lt > 0.0f ? (FP8 ? a.v_scale : 1.0f) / lt : 0.0f;
+    const float lse2 = FOLD ? lse_fold : lt > 0.0f ? st.m + log2f(lt) : -INFINITY;
+    const bool write_final = FOLD || it.slot < 0;
     // The outputs go out through LDS (the K/V stages are free after the last
     // block barrier; each wave uses its own region): the wave writes its
     // O^T fragments as rows, 16-byte chunk c of row r at position
@@ -1009,7 +1114,7 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
         orow = (size_t)(it.q_tok0 + tk) * a.num_qo_heads + it.kv_head * g + (R - tk * g);
         return tk < it.n_tok;
     };
-    if (R16 && it.slot < 0) {
+    if (R16 && write_final) {
         // 16-row waves: acc[dt][i] is d = 16 dt + 4 part + i of row qc, so a
         // 16-byte chunk 2 dt + part / 2 is written by lanes part and part ^ 1
         constexpr int CPR = T::CPR;
@@ -1069,7 +1174,7 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
         }
         if (row_valid && part == 0)
             a.part_lse[(size_t)it.slot * kTileRows + r] = lse2;
-    } else if (it.slot < 0) {
+    } else if (write_final) {
         constexpr int CPR = T::CPR;          // 16-byte chunks per bf16 row
         constexpr int RPI = 64 / CPR;        // rows per read instruction
         char *wl = smem + w * (32 * T::RB);
@@ -1150,17 +1255,34 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem)
     }
 }
 
-template <int HD, bool PAGED, bool FP8>
+// FOLDK: the instance that also runs fold items (it is built in its own
+// translation unit; the extra path costs registers, so plans without fold
+// items launch the plain instance).
+template <int HD, bool PAGED, bool FP8, bool FOLDK>
 __global__ __launch_bounds__(Tile<HD>::THREADS, HD == 128 ? 2 : 1) void tile_kernel(TileArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const Item it = a.items[blockIdx.x];
     if (it.n_tok == 0)
         return;  // padding item of the launch order
+    if constexpr (FOLDK) {
+        if (it.fold_keys > 0) {
+            // in-workgroup chunk folding: the tile's canonical KV chunks in
+            // order (the running state is carried in the item's slot)
+            const int n = (it.key_end - it.key_begin + it.fold_keys - 1) / it.fold_keys;
+            for (int fc = 0; fc < n; ++fc) {
+                if (a.scale_log2 > 0.0f)
+                    tile_body<HD, true, PAGED, FP8, true>(a, it, smem, fc);
+                else
+                    tile_body<HD, false, PAGED, FP8, true>(a, it, smem, fc);
+            }
+            return;
+        }
+    }
     if (a.scale_log2 > 0.0f)
-        tile_body<HD, true, PAGED, FP8>(a, it, smem);
+        tile_body<HD, true, PAGED, FP8, false>(a, it, smem, 0);
     else
-        tile_body<HD, false, PAGED, FP8>(a, it, smem);
+        tile_body<HD, false, PAGED, FP8, false>(a, it, smem, 0);
 }
 
 // dynamic LDS of a tile kernel instance: the K/V stages, the fp8 staging
@@ -1168,6 +1290,7 @@ __global__ __launch_bounds__(Tile<HD>::THREADS, HD == 128 ? 2 : 1) void tile_ker
 template <int HD, bool FP8>
 constexpr int tile_lds_bytes() { return Tile<HD>::LDS_BYTES + (FP8 ? 2 * Tile<HD>::BK * HD : 0) + 4 * Tile<HD>::NW; }
 
+#if !RP_TILE_FOLD
 template <int HD>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a)
 {
@@ -1192,7 +1315,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a)
             const float4 *src = reinterpret_cast<const float4 *>(a.part_o + (slot * kTileRows + r) * HD + 8 * cc);
             const float4 x0 = src[0], x1 = src[1];
             const float o_c[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-            fold_state<8>(lse_run, o_run, lse_c, o_c);
+            const FoldWeights fw = fold_weights(lse_run, lse_c);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                o_run[e] = fold_value(fw, o_run[e], o_c[e]);
+            lse_run = fw.lse;
         }
         const int tok = r / a.group;
         const int head = it.kv_head * a.group + (r - tok * a.group);
@@ -1207,11 +1334,14 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a)
     }
 }
 
+#endif
+
 template <int HD, bool PAGED, bool FP8>
 int launch_tile(const TileArgs &args, int64_t num_items, hipStream_t stream)
 {
+    constexpr bool FOLDK = RP_TILE_FOLD != 0;
     constexpr int lds = tile_lds_bytes<HD, FP8>();
-    const void *fn = reinterpret_cast<const void *>(&tile_kernel<HD, PAGED, FP8>);
+    const void *fn = reinterpret_cast<const void *>(&tile_kernel<HD, PAGED, FP8, FOLDK>);
     // The dynamic-LDS limit is a per-device function attribute: set it once
     // per device (devices beyond 64 set it at every launch).
     static std::atomic<unsigned long long> attr_devices{0};
@@ -1226,16 +1356,25 @@ int launch_tile(const TileArgs &args, int64_t num_items, hipStream_t stream)
             return (int)e;
         attr_devices.fetch_or(bit, std::memory_order_release);
     }
-    auto kernel = tile_kernel<HD, PAGED, FP8>;
+    auto kernel = tile_kernel<HD, PAGED, FP8, FOLDK>;
     hipLaunchKernelGGL(kernel, dim3((unsigned)num_items), dim3(Tile<HD>::THREADS), lds, stream, args);
     return (int)hipGetLastError();
 }
 
 }  // namespace
 
-int launch_tile_kernel(int head_dim, bool paged, bool fp8, const TileArgs &args, int64_t num_items,
-                       void *stream)
+#if RP_TILE_FOLD
+int launch_tile_fold_kernel(int head_dim, bool paged, bool fp8, const TileArgs &args, int64_t num_items,
+                            void *stream)
+#else
+int launch_tile_kernel(int head_dim, bool paged, bool fp8, bool fold, const TileArgs &args,
+                       int64_t num_items, void *stream)
+#endif
 {
+#if !RP_TILE_FOLD
+    if (fold)
+        return launch_tile_fold_kernel(head_dim, paged, fp8, args, num_items, stream);
+#endif
     if (num_items <= 0)
         return (int)hipSuccess;
     if (num_items > INT_MAX)
@@ -1256,6 +1395,7 @@ int launch_tile_kernel(int head_dim, bool paged, bool fp8, const TileArgs &args,
     return (int)hipErrorInvalidValue;
 }
 
+#if !RP_TILE_FOLD
 int launch_merge_kernel(int head_dim, const MergeArgs &args, int64_t num_items, void *stream)
 {
     if (num_items <= 0)
@@ -1271,5 +1411,7 @@ int launch_merge_kernel(int head_dim, const MergeArgs &args, int64_t num_items, 
         return (int)hipErrorInvalidValue;
     return (int)hipGetLastError();
 }
+
+#endif
 
 }  // namespace rp

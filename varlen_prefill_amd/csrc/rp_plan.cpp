@@ -2,10 +2,14 @@
 //
 // Tiles: each request's query tokens are cut into tiles of kTileRows / g
 // tokens (g = GQA group size), one tile per (token range, kv head).  KV is cut
-// into canonical chunks of kv_chunk keys at request-relative offsets; a tile
-// whose visible keys reach past one chunk gets one work item per chunk, each
-// writing an fp32 partial state, and one merge item (split-KV, page "vllm-rlt
-// PR #112", results notes: split-KV parallelism pays off for few requests).
+// into canonical chunks of kv_chunk keys at request-relative offsets.  A tile
+// whose visible keys reach past one chunk is either split (one work item per
+// chunk, each writing an fp32 partial state, and one merge item: split-KV,
+// page "vllm-rlt PR #112", results notes: split-KV parallelism pays off for
+// few requests) or folded (one work item that runs the chunks in order and
+// folds their states itself).  Both give the same bits; the split mode (or,
+// in the automatic mode, whether the grid fills the GPU without splitting)
+// picks the placement.
 // Items are ordered longest-first (LPT), so the hardware's in-order workgroup
 // dispatch approximates greedy longest-processing-time scheduling.
 //
@@ -63,8 +67,8 @@ void order_items(std::vector<Item> &items, int xcds)
     std::vector<std::vector<Item>> lists((size_t)xcds);
     std::map<std::tuple<int, int, int, int>, int> home;  // (request, kv head, chunk, split) -> XCD
     for (const Item &it : items) {
-        const auto key = std::make_tuple(it.request, it.kv_head, it.slot >= 0 ? it.chunk : 0,
-                                         it.slot >= 0 ? 1 : 0);
+        const bool partial = it.slot >= 0 && it.fold_keys == 0;
+        const auto key = std::make_tuple(it.request, it.kv_head, partial ? it.chunk : 0, partial ? 1 : 0);
         auto h = home.find(key);
         int x;
         if (h != home.end() && load[(size_t)h->second] + it.cost <= target) {
@@ -156,8 +160,8 @@ int build_plan(const int32_t *q_indptr, const int32_t *kv_indptr, const PlanShap
         err = "num_xcds must be in [1, 64] (0 = default)";
         return kEInval;
     }
-    if (shape.split_mode != 0 && shape.split_mode != 2) {
-        err = "unknown split_mode (0 = auto, 2 = always)";
+    if (shape.split_mode < 0 || shape.split_mode > 2) {
+        err = "unknown split_mode (0 = auto, 1 = never, 2 = always)";
         return kEInval;
     }
     if (shape.batch > 0 && (q_indptr == nullptr || kv_indptr == nullptr)) {
@@ -190,6 +194,25 @@ int build_plan(const int32_t *q_indptr, const int32_t *kv_indptr, const PlanShap
         plan.total_kv = (int64_t)kv_indptr[shape.batch] - kv_indptr[0];
     }
 
+    // cost of a work item over keys [k0, k1): two MFMA halves per key block,
+    // one more where the kernel is expected to split P (tiles whose rows see
+    // few keys), plus a fixed epilogue share
+    auto item_cost = [&](int64_t k0, int64_t k1, int64_t lim_first) {
+        int64_t cost = 4;
+        if (k1 > k0)
+            cost += ((k1 + bk - 1) / bk - k0 / bk) * (lim_first <= kHiLoKeys ? 3 : 2);
+        return cost;
+    };
+    // tiles in batch order: (tile item over all its keys, chunk size, chunk
+    // count); multi-chunk tiles are split or folded below
+    struct TileKeys {
+        Item it;
+        int64_t C;
+        int64_t n_chunks;
+    };
+    std::vector<TileKeys> tiles;
+    int64_t total_cost = 0, max_fold_cost = 0;
+
     double pairs_total = 0.0;
     for (int b = 0; b < shape.batch; ++b) {
         const int64_t qo = (int64_t)q_indptr[b + 1] - q_indptr[b];
@@ -205,7 +228,9 @@ int build_plan(const int32_t *q_indptr, const int32_t *kv_indptr, const PlanShap
             const int64_t lim_last = limit_of(t0 + n_tok - 1, qo, kv, causal);
             const int64_t key_end = lim_last;
             const int64_t n_chunks = key_end > 0 ? (key_end + C - 1) / C : 0;
-            const bool split = n_chunks > 1;  // AUTO and ALWAYS: split every multi-chunk tile
+            int64_t cost = 0;   // summed over the chunks (the folded item's cost)
+            for (int64_t ch = 0; ch < std::max<int64_t>(n_chunks, 1); ++ch)
+                cost += item_cost(ch * C, std::min<int64_t>((ch + 1) * C, key_end), lim_first);
             for (int kvh = 0; kvh < shape.num_kv_heads; ++kvh) {
                 Item it{};
                 it.q_tok0 = (int32_t)(q_indptr[b] + t0);
@@ -217,34 +242,55 @@ int build_plan(const int32_t *q_indptr, const int32_t *kv_indptr, const PlanShap
                 it.kv_head = kvh;
                 it.request = b;
                 it.lim_first = (int32_t)lim_first;
-                if (!split) {
-                    it.key_begin = 0;
-                    it.key_end = (int32_t)key_end;
-                    it.slot = -1;
-                    it.chunk = (int32_t)n_chunks;
-                    plan.items.push_back(it);
-                } else {
-                    const int64_t slot0 = plan.num_slots;
-                    plan.num_slots += n_chunks;
-                    for (int64_t ch = 0; ch < n_chunks; ++ch) {
-                        Item pi = it;
-                        pi.key_begin = (int32_t)(ch * C);
-                        pi.key_end = (int32_t)std::min<int64_t>((ch + 1) * C, key_end);
-                        pi.slot = (int32_t)(slot0 + ch);
-                        pi.chunk = (int32_t)ch;
-                        plan.items.push_back(pi);
-                        ++plan.num_partial_items;
-                    }
-                    MergeItem mi{};
-                    mi.q_tok0 = it.q_tok0;
-                    mi.n_tok = it.n_tok;
-                    mi.kv_head = kvh;
-                    mi.slot0 = (int32_t)slot0;
-                    mi.n_chunks = (int32_t)n_chunks;
-                    mi.request = b;
-                    plan.merges.push_back(mi);
-                }
+                it.key_begin = 0;
+                it.key_end = (int32_t)key_end;
+                it.chunk = (int32_t)n_chunks;
+                it.slot = -1;
+                tiles.push_back({it, C, n_chunks});
+                total_cost += cost;
+                if (n_chunks > 1)
+                    max_fold_cost = std::max(max_fold_cost, cost);
             }
+        }
+    }
+
+    // placement of the multi-chunk tiles: RP_SPLIT_NEVER folds, RP_SPLIT_ALWAYS
+    // splits, the automatic mode folds at head_dim 128 when the grid fills the
+    // GPU without split-KV
+    bool fold = shape.split_mode == 1;
+    if (shape.split_mode == 0)
+        fold = shape.head_dim == 128 && max_fold_cost * kResidentTiles128 <= total_cost;
+    for (const TileKeys &tk : tiles) {
+        const Item &it = tk.it;
+        if (tk.n_chunks <= 1) {
+            plan.items.push_back(it);
+        } else if (fold) {
+            Item fi = it;
+            fi.slot = (int32_t)plan.num_slots;
+            fi.fold_keys = (int32_t)tk.C;
+            plan.num_slots += 1;
+            plan.items.push_back(fi);
+            ++plan.num_fold_items;
+        } else {
+            const int64_t slot0 = plan.num_slots;
+            plan.num_slots += tk.n_chunks;
+            for (int64_t ch = 0; ch < tk.n_chunks; ++ch) {
+                Item pi = it;
+                pi.key_begin = (int32_t)(ch * tk.C);
+                pi.key_end = (int32_t)std::min<int64_t>((ch + 1) * tk.C, it.key_end);
+                pi.slot = (int32_t)(slot0 + ch);
+                pi.chunk = (int32_t)ch;
+                plan.items.push_back(pi);
+                ++plan.num_partial_items;
+            }
+            MergeItem mi{};
+            mi.q_tok0 = it.q_tok0;
+            mi.n_tok = it.n_tok;
+            mi.kv_head = it.kv_head;
+            mi.slot0 = (int32_t)slot0;
+            mi.n_chunks = (int32_t)tk.n_chunks;
+            mi.request = it.request;
+            plan.merges.push_back(mi);
         }
     }
     if (plan.num_slots > (int64_t)INT32_MAX / kTileRows) {
@@ -252,15 +298,13 @@ int build_plan(const int32_t *q_indptr, const int32_t *kv_indptr, const PlanShap
         return kEUnsupported;
     }
 
-    // cost: two MFMA halves per key block, one more where the kernel is
-    // expected to split P (tiles whose rows see few keys), plus a fixed
-    // epilogue share
     for (Item &it : plan.items) {
-        int64_t cost = 4;
-        if (it.key_end > it.key_begin) {
-            const int64_t kb0 = it.key_begin / bk;
-            const int64_t kb1 = (it.key_end + bk - 1) / bk;
-            cost += (kb1 - kb0) * (it.lim_first <= kHiLoKeys ? 3 : 2);
+        int64_t cost = 0;
+        if (it.fold_keys > 0) {
+            for (int64_t k0 = it.key_begin; k0 < it.key_end; k0 += it.fold_keys)
+                cost += item_cost(k0, std::min<int64_t>(k0 + it.fold_keys, it.key_end), it.lim_first);
+        } else {
+            cost = item_cost(it.key_begin, it.key_end, it.lim_first);
         }
         it.cost = (int32_t)std::min<int64_t>(cost, INT32_MAX);
     }

@@ -27,6 +27,7 @@ struct HostPlan {
     std::vector<MergeItem> merges;
     int64_t num_slots = 0;
     int64_t num_partial_items = 0;
+    int64_t num_fold_items = 0;  // items that fold their tile's KV chunks in the workgroup
     int64_t total_q = 0;
     int64_t total_kv = 0;
     int64_t max_q_row = 0;   // q_indptr[batch]: rows Q/O must hold
