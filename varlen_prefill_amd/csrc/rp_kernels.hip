@@ -890,7 +890,8 @@ __device__ inline void tile_body(const TileArgs &a, const Item &it, char *smem, 
 #pragma unroll
     for (int ds = 0; ds < NQF; ++ds)
         asm volatile("" :: "v"(st.qf[ds]));
-    constexpr int NACC = sizeof(st.acc) / sizeof(float);   // accumulator floats per lane
+    constexpr int NACC = R16 ? 4 * T::DT16 : 16 * T::DB;   // accumulator floats per lane
+    static_assert(NACC * sizeof(float) == sizeof(st.acc), "accumulator layout");
     auto acc_at = [&](int i) __attribute__((always_inline)) -> float {
         if constexpr (R16)
             return st.acc[i / 4][i % 4];
