@@ -187,6 +187,48 @@ def test_shared_prefix_empty_prefix_is_rp_run_bitwise():
 
 
 @pytest.mark.parametrize("case", [
+    # qo, own kv, shared len, Hq, Hkv, D, causal, kv_chunk, split mode
+    ([30, 130, 1, 0, 64], [30, 200, 5, 9, 64], 700, 32, 8, 128, True, 0, "auto"),
+    ([17, 90], [17, 300], 1000, 16, 4, 256, True, 0, "auto"),
+    ([40, 300, 3], [700, 300, 1000], 500, 8, 2, 128, True, 128, "always"),   # merge kernel path
+    ([40, 300, 3], [700, 300, 1000], 500, 8, 2, 128, True, 128, "never"),    # fold items
+    ([40, 100], [700, 1000], 300, 8, 2, 256, False, 128, "always"),
+])
+def test_shared_prefix_equals_two_runs_and_merge_bitwise(case):
+    """Shared-prefix attention is bit-identical to running both levels as
+    ordinary plans and merging them with merge_state, whatever the own
+    level's placement (final items, split items + merge kernel, fold items),
+    with and without the LSE output."""
+    import varlen_prefill_amd as vp
+    qo, kv, p, hq, hkv, d, causal, chunk, mode = case
+    split_mode = {"auto": vp.RP_SPLIT_AUTO, "always": vp.RP_SPLIT_ALWAYS,
+                  "never": vp.RP_SPLIT_NEVER}[mode]
+    b = make_batch(qo, kv, hq, hkv, d, seed=900 + p, q_base=2)
+    _, ks, vs = request_tensors(900 + p, 10**6, 0, p, hq, hkv, d)
+    sm = default_scale(d)
+    q, ksd, vsd = b.q.to(DEV), ks.to(DEV), vs.to(DEV)
+    kd, vd = b.k.to(DEV), b.v.to(DEV)
+    sp = vp.SharedPrefixPlan(b.q_indptr, b.kv_indptr, p, hq, hkv, d, causal, kv_chunk=chunk,
+                             split_mode=split_mode)
+    of, lf = sp.run(q, ksd, vsd, kd, vd, sm_scale=sm)
+    of, lf = of.clone(), lf.clone()
+    on, ln = sp.run(q, ksd, vsd, kd, vd, sm_scale=sm, return_lse=False)   # no LSE output
+    assert ln is None
+    q0, q1 = int(b.q_indptr[0]), int(b.q_indptr[-1])
+    assert torch.equal(on[q0:q1].view(torch.int16), of[q0:q1].view(torch.int16))
+    lvl1 = vp.Plan([0, q1 - q0], [0, p], hq, hkv, d, False, kv_chunk=chunk, split_mode=split_mode)
+    o1, l1 = lvl1.run(q[q0:q1].contiguous(), ksd, vsd, sm_scale=sm)
+    lvl2 = vp.Plan(b.q_indptr, b.kv_indptr, hq, hkv, d, causal, kv_chunk=chunk, split_mode=split_mode)
+    o2, l2 = lvl2.run(q, kd, vd, sm_scale=sm)
+    om, lm = vp.merge_state(o1, l1, o2[q0:q1].contiguous(), l2[q0:q1].contiguous())
+    torch.cuda.synchronize()
+    for x in (sp, lvl1, lvl2):
+        x.close()
+    assert torch.equal(of[q0:q1].view(torch.int16), om.view(torch.int16))
+    assert torch.equal(lf[q0:q1].view(torch.int32), lm.view(torch.int32))
+
+
+@pytest.mark.parametrize("case", [
     # qo, own kv, shared len, Hq, Hkv, D, causal, page size
     ([30, 130, 1, 0, 64], [30, 200, 5, 9, 64], 700, 32, 8, 128, True, 16),
     ([17, 90], [17, 300], 1000, 16, 4, 256, True, 64),
