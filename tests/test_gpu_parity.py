@@ -478,3 +478,30 @@ def test_reference_max_moves(mode):
         import varlen_prefill_amd as vp
         plan_kw.update(kv_chunk=128, split_mode=vp.RP_SPLIT_NEVER)
     _check_full(b, True, sm, **plan_kw)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes_every_placement(seed):
+    """Seeded random ragged batches (request count, lengths with qo <= kv and
+    qo > kv, empty requests, GQA group 1..8, head_dim 128/256, causal or
+    not, canonical chunks of 64..320 keys): the fold placement (NEVER)
+    against the oracle at the standard gates, and NEVER, ALWAYS and AUTO
+    bit for bit."""
+    import varlen_prefill_amd as vp
+    rng = np.random.default_rng(4000 + seed)
+    n = int(rng.integers(1, 6))
+    qo = [int(x) for x in rng.integers(0, 200, n)]
+    kv = [int(x) if rng.random() < 0.8 else int(q) for x, q in zip(rng.integers(0, 900, n), qo)]
+    g = int(rng.choice([1, 2, 4, 8]))
+    hkv = int(rng.choice([1, 2]))
+    d = int(rng.choice([128, 256]))
+    causal = bool(rng.random() < 0.7)
+    chunk = int(rng.choice([64, 128, 192, 320]))
+    b = make_batch(qo, kv, g * hkv, hkv, d, seed=4000 + seed, q_base=int(rng.integers(0, 3)))
+    sm = default_scale(d)
+    print(f"qo={qo} kv={kv} g={g} hkv={hkv} d={d} causal={causal} chunk={chunk}", flush=True)
+    o, lse, _ = _check_full(b, causal, sm, kv_chunk=chunk, split_mode=vp.RP_SPLIT_NEVER)
+    for mode in (vp.RP_SPLIT_ALWAYS, vp.RP_SPLIT_AUTO):
+        o2, l2 = _gpu(b, causal, sm, kv_chunk=chunk, split_mode=mode)
+        assert torch.equal(o2.view(torch.int16), o.view(torch.int16)), mode
+        assert torch.equal(l2.view(torch.int32), lse.view(torch.int32)), mode
