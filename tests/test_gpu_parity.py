@@ -505,3 +505,27 @@ def test_random_shapes_every_placement(seed):
         o2, l2 = _gpu(b, causal, sm, kv_chunk=chunk, split_mode=mode)
         assert torch.equal(o2.view(torch.int16), o.view(torch.int16)), mode
         assert torch.equal(l2.view(torch.int32), lse.view(torch.int32)), mode
+
+
+EXTREME = [
+    # qo, kv, Hq, Hkv, D, causal
+    ([3, 1, 2], [70000, 1, 0], 128, 1, 128, True),     # GQA group 128 (one token per tile), 35 decode chunks
+    ([300], [70000], 8, 1, 128, True),                 # 9 canonical chunks of 8192 keys per tile
+    ([64, 5, 40], [64, 300, 9000], 64, 4, 256, True),  # group 16 at head_dim 256 (8 tokens per tile)
+    ([33], [20000], 16, 2, 256, False),                # non-causal, 3 chunks at head_dim 256
+]
+
+
+@pytest.mark.parametrize("case", range(len(EXTREME)))
+def test_extreme_shapes(case):
+    """Largest GQA groups, very long KV (tens of canonical chunks) and
+    non-causal long KV: every row against the oracle in the fold placement,
+    and split and fold placements bit for bit."""
+    import varlen_prefill_amd as vp
+    qo, kv, hq, hkv, d, causal = EXTREME[case]
+    b = make_batch(qo, kv, hq, hkv, d, seed=5000 + case)
+    sm = default_scale(d)
+    o, lse, _ = _check_full(b, causal, sm, split_mode=vp.RP_SPLIT_NEVER)
+    o2, l2 = _gpu(b, causal, sm, split_mode=vp.RP_SPLIT_ALWAYS)
+    assert torch.equal(o2.view(torch.int16), o.view(torch.int16))
+    assert torch.equal(l2.view(torch.int32), lse.view(torch.int32))
