@@ -340,11 +340,17 @@ def test_injected_allocation_failure_leaves_outputs_untouched(monkeypatch):
     compare(bf16_to_f64(out.cpu()), lse.cpu().double().numpy(), ro, rl)
 
 
-def test_graph_capture_replays():
+@pytest.mark.parametrize("mode", ["auto", "never"])
+def test_graph_capture_replays(mode):
+    """A captured rp_run replays bit-identically (split items + merge kernel,
+    or fold items whose running state lives in the workspace), with eager
+    work and synchronisations between the replays."""
     import varlen_prefill_amd as vp
+    split_mode = vp.RP_SPLIT_NEVER if mode == "never" else vp.RP_SPLIT_AUTO
     b = make_batch([150, 20], [900, 20], 8, 2, 128, seed=12)
     q, k, v = b.q.to(DEV), b.k.to(DEV), b.v.to(DEV)
-    plan = vp.Plan(b.q_indptr, b.kv_indptr, 8, 2, 128, True, kv_chunk=256)
+    plan = vp.Plan(b.q_indptr, b.kv_indptr, 8, 2, 128, True, kv_chunk=256, split_mode=split_mode)
+    assert (plan.info["num_fold_items"] > 0) == (mode == "never")
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[0], 8, dtype=torch.float32, device=DEV)
     ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=DEV)
@@ -361,6 +367,7 @@ def test_graph_capture_replays():
     for _ in range(3):
         out.fill_(float("nan"))
         lse.fill_(float("nan"))
+        ws.fill_(0xA5)   # stale workspace contents must not matter
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
